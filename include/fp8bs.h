@@ -1,0 +1,156 @@
+/*
+ * fp8bs.h -- C ABI of the MI355X (gfx950) fine-grained FP8 block-scaled GEMM
+ * library, libfp8bs.so.
+ *
+ * What the library computes is the FP8 GEMM of the DeepSeek-V3 technical
+ * report, section 3.3.2 "Improved Precision from Quantization and
+ * Multiplication", as paraphrased on the innerforce.co.kr and
+ * why-be.why-be.co.kr pages (and again on the page headed "Deepseek : The
+ * Ultimate Convenience!"):
+ *   - tensors are quantized to E4M3 (4-bit exponent, 3-bit mantissa) in small
+ *     groups, each group sharing one scaling factor, for all of Fprop, Dgrad
+ *     and Wgrad;
+ *   - the groups lie along the inner (K) dimension of the GEMM;
+ *   - the FP8 product is formed one K interval at a time, each interval's
+ *     partial result is promoted to FP32 and accumulated there in full FP32
+ *     precision (report Figure 7(b)).
+ * Readings where the pages are silent: OCP E4M3FN codes (bias 7, max 448, no
+ * infinities), scale = amax/448 as an FP32 (1.0 for an all-zero group),
+ * codes = E4M3_RNE_saturating(x / scale) with IEEE FP32 division, groups of
+ * 1x128 (activations), 128x128 (weights) and 128x1 (Wgrad operands, written
+ * transposed), promotion interval 128, BF16 output rounded to nearest even.
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers to caller-allocated, contiguous,
+ *     row-major memory, 16-byte aligned. The library allocates nothing, keeps
+ *     no state between calls and is safe to call from several host threads.
+ *   - `stream` is a hipStream_t (NULL = the default stream). Work is enqueued
+ *     asynchronously; nothing synchronizes inside the library.
+ *   - Return value: FP8BS_OK (0) or a negative fp8bs_status. Arguments are
+ *     validated on the host before anything is enqueued; on an error nothing
+ *     is enqueued and the outputs are untouched. FP8BS_ERR_LAUNCH reports a
+ *     launch failure from the HIP runtime. Faults inside a kernel (e.g. from
+ *     device offsets that break their precondition) surface at the caller's
+ *     next synchronization.
+ *   - E4M3 codes are stored as uint8; BF16 as its uint16 bit pattern;
+ *     scales as float32. `dtype` selects the high-precision input type.
+ *   - Inputs must be finite; the result for NaN/Inf inputs is unspecified.
+ */
+#ifndef FP8BS_H
+#define FP8BS_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FP8BS_ABI_VERSION 1
+
+/* High-precision input type of the quantizers. */
+enum fp8bs_dtype { FP8BS_F32 = 0, FP8BS_BF16 = 1 };
+
+/* How the GEMM reads the B operand's scales (see fp8_gemm_blockscaled). */
+enum fp8bs_scale_mode { FP8BS_SCALE_BLOCK128 = 0, FP8BS_SCALE_ROW = 1 };
+
+enum fp8bs_status {
+  FP8BS_OK = 0,
+  FP8BS_ERR_NULL_PTR = -1, /* a required pointer is NULL                      */
+  FP8BS_ERR_SHAPE = -2,    /* negative size or a size not a multiple of 128   */
+  FP8BS_ERR_ALIGN = -3,    /* a pointer is not 16-byte aligned                */
+  FP8BS_ERR_DTYPE = -4,    /* unknown dtype                                   */
+  FP8BS_ERR_MODE = -5,     /* unknown scale mode, or qT/sT given one-sided    */
+  FP8BS_ERR_LAUNCH = -6,   /* the HIP runtime rejected a kernel launch        */
+  FP8BS_ERR_TOO_LARGE = -7 /* a size exceeds the 32-bit index range supported */
+};
+
+/*
+ * Activation quantization, one group per (row m, 128-wide K chunk kb):
+ * report section 3.3.2 (fine-grained grouping along K), innerforce.co.kr page.
+ *   x  [M][K]      F32 or BF16 (dtype)
+ *   q  [M][K]      uint8 E4M3 codes
+ *   s  [K/128][M]  float32, s[kb][m] = amax(group)/448, 1.0 for a zero group
+ * K must be a multiple of 128; any M >= 0 (M == 0 or K == 0: no-op).
+ */
+int fp8_quant_act_1x128(const void* x, int dtype, int64_t M, int64_t K,
+                        uint8_t* q, float* s, void* stream);
+
+/*
+ * Weight quantization, one group per 128x128 block (nb, kb): report section
+ * 3.3.2, innerforce.co.kr page. Optionally also writes the transposed copy
+ * used by Dgrad (the pages call a transposition fused into the GEMM
+ * cumbersome, report section 3.5.2, "Deepseek : The Ultimate Convenience!").
+ *   w   [N][K]           F32 or BF16 (dtype)
+ *   q   [N][K]           uint8 codes
+ *   s   [N/128][K/128]   float32
+ *   qT  [K][N]           uint8, qT = q^T        (NULL: not written)
+ *   sT  [K/128][N/128]   float32, sT = s^T      (NULL: not written)
+ * qT and sT must be both given or both NULL. N and K multiples of 128.
+ */
+int fp8_quant_w_128x128(const void* w, int dtype, int64_t N, int64_t K,
+                        uint8_t* q, float* s, uint8_t* qT, float* sT,
+                        void* stream);
+
+/*
+ * Wgrad-operand quantization, one group per (token chunk tb, channel c):
+ * 128 consecutive tokens of one channel, so that the Wgrad GEMM, which
+ * contracts over tokens, again has its groups along its inner dimension
+ * (report sections 3.3.1-3.3.2: the FP8 Wgrad GEMM). The codes are written
+ * transposed so that the GEMM reads K-contiguous rows.
+ *   x   [M][C]       F32 or BF16 (dtype); M = tokens, C = channels
+ *   qT  [C][M]       uint8 codes, qT[c][t] encodes x[t][c]
+ *   sT  [M/128][C]   float32
+ * M must be a multiple of 128; any C >= 0.
+ */
+int fp8_quant_act_128x1_T(const void* x, int dtype, int64_t M, int64_t C,
+                          uint8_t* qT, float* sT, void* stream);
+
+/*
+ * Block-scaled FP8 GEMM with per-chunk FP32 promotion (report section 3.3.2
+ * and Figure 7(b); why-be.why-be.co.kr and innerforce.co.kr pages):
+ *   C[m][n] = bf16( sum_kb sA[kb][m] * sb(kb,n) * sum_{k in kb} A[m][k]*B[n][k] )
+ * where each inner sum is an FP8 product accumulated in FP32 over one 128-wide
+ * chunk, then promoted: scaled and added to an FP32 accumulator.
+ *   A   [M][K]  uint8 codes (K contiguous)      sA [K/128][M] float32
+ *   B   [N][K]  uint8 codes (K contiguous)      sB see mode
+ *   b_scale_mode FP8BS_SCALE_BLOCK128: sB[N/128][K/128], sb(kb,n) = sB[n/128][kb]
+ *                  (Fprop with W; Dgrad with the transposed weight copy)
+ *                FP8BS_SCALE_ROW:      sB[K/128][N],     sb(kb,n) = sB[kb][n]
+ *                  (Wgrad with both operands from fp8_quant_act_128x1_T)
+ *   C   [M][N]  BF16 bits, round to nearest even
+ * K and N multiples of 128; any M >= 0. M*K, N*K and M*N below 2^31.
+ */
+int fp8_gemm_blockscaled(const uint8_t* A, const float* sA, const uint8_t* B,
+                         const float* sB, int b_scale_mode, uint16_t* C,
+                         int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
+ * Grouped (per-expert) form for MoE experts (report sections 3.3.2 and
+ * 3.4.2; per-expert token batches, small in decoding, on the page headed
+ * "Deepseek : The Ultimate Convenience!"): the rows [off[e], off[e+1]) of A
+ * are multiplied by expert e's weights, block scale mode.
+ *   A   [M_total][K]         uint8     sA [K/128][M_total] float32
+ *   B   [E][N][K]            uint8     sB [E][N/128][K/128] float32
+ *   C   [M_total][N]         BF16 bits
+ *   group_offsets  DEVICE int32[E+1], off[0] = 0, non-decreasing,
+ *                  off[E] = M_total (precondition, not checked on the host;
+ *                  the kernels clamp every row index into [0, M_total)).
+ * K and N multiples of 128; E >= 0; M_total >= 0.
+ */
+int fp8_grouped_gemm_blockscaled(const uint8_t* A, const float* sA,
+                                 const uint8_t* B, const float* sB,
+                                 uint16_t* C, const int32_t* group_offsets,
+                                 int E, int64_t M_total, int64_t N, int64_t K,
+                                 void* stream);
+
+/* Human-readable name of a status code (static string). */
+const char* fp8bs_status_string(int status);
+
+/* FP8BS_ABI_VERSION of the loaded library. */
+int fp8bs_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8BS_H */
