@@ -1,0 +1,184 @@
+"""ctypes binding of libfp8bs.so: argument marshalling only.
+
+Every function here has the name of the C entry point it calls. It checks the
+torch tensors it is given (device, dtype, contiguity), allocates the outputs
+with torch on the input's device, and calls the library on the current torch
+stream. All arithmetic happens in the HIP kernels; there is no fallback: if the
+library is missing or a call fails, an exception is raised.
+"""
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfp8bs.so")
+
+F32, BF16 = 0, 1
+SCALE_BLOCK128, SCALE_ROW = 0, 1
+ABI_VERSION = 1
+
+_c_int64 = ctypes.c_int64
+_vp = ctypes.c_void_p
+
+_SIGNATURES = {
+    "fp8_quant_act_1x128": [_vp, ctypes.c_int, _c_int64, _c_int64, _vp, _vp, _vp],
+    "fp8_quant_w_128x128": [_vp, ctypes.c_int, _c_int64, _c_int64, _vp, _vp, _vp, _vp, _vp],
+    "fp8_quant_act_128x1_T": [_vp, ctypes.c_int, _c_int64, _c_int64, _vp, _vp, _vp],
+    "fp8_gemm_blockscaled": [_vp, _vp, _vp, _vp, ctypes.c_int, _vp, _c_int64, _c_int64, _c_int64, _vp],
+    "fp8_grouped_gemm_blockscaled": [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _c_int64, _c_int64,
+                                     _c_int64, _vp],
+    "fp8bs_status_string": [ctypes.c_int],
+    "fp8bs_abi_version": [],
+}
+
+_lib = None
+
+
+class Fp8bsError(RuntimeError):
+    def __init__(self, fn, status):
+        super().__init__(f"{fn} failed: {status} ({status_string(status)})")
+        self.status = status
+
+
+def lib():
+    """The loaded library (loaded on first use; raises if it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run `python -m fp8_block_scaled_x1_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, args in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.argtypes = args
+            fn.restype = ctypes.c_char_p if name == "fp8bs_status_string" else ctypes.c_int
+        if handle.fp8bs_abi_version() != ABI_VERSION:
+            raise ImportError(f"libfp8bs ABI {handle.fp8bs_abi_version()} != {ABI_VERSION}")
+        _lib = handle
+    return _lib
+
+
+def status_string(status):
+    return lib().fp8bs_status_string(int(status)).decode()
+
+
+def _check(fn, status):
+    if status != 0:
+        raise Fp8bsError(fn, status)
+
+
+def _stream(t):
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _dev(t, name, dtypes):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU (got {t.device})")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _in_dtype(x):
+    return {torch.float32: F32, torch.bfloat16: BF16}[x.dtype]
+
+
+def fp8_quant_act_1x128(x):
+    """x[M][K] f32|bf16 -> (q uint8 [M][K], s float32 [K/128][M])."""
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D")
+    M, K = x.shape
+    px = _dev(x, "x", (torch.float32, torch.bfloat16))
+    q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    s = torch.empty((K // 128 if K % 128 == 0 else 0, M), dtype=torch.float32, device=x.device)
+    _check("fp8_quant_act_1x128",
+           lib().fp8_quant_act_1x128(px, _in_dtype(x), M, K, q.data_ptr(), s.data_ptr(), _stream(x)))
+    return q, s
+
+
+def fp8_quant_w_128x128(w, transposed=False):
+    """w[N][K] -> (q[N][K], s[N/128][K/128]) and, if transposed, (qT[K][N], sT[K/128][N/128])."""
+    if w.dim() != 2:
+        raise ValueError("w must be 2-D")
+    N, K = w.shape
+    pw = _dev(w, "w", (torch.float32, torch.bfloat16))
+    q = torch.empty((N, K), dtype=torch.uint8, device=w.device)
+    s = torch.empty((N // 128, K // 128), dtype=torch.float32, device=w.device)
+    qT = sT = None
+    if transposed:
+        qT = torch.empty((K, N), dtype=torch.uint8, device=w.device)
+        sT = torch.empty((K // 128, N // 128), dtype=torch.float32, device=w.device)
+    _check("fp8_quant_w_128x128",
+           lib().fp8_quant_w_128x128(pw, _in_dtype(w), N, K, q.data_ptr(), s.data_ptr(),
+                                     qT.data_ptr() if qT is not None else None,
+                                     sT.data_ptr() if sT is not None else None, _stream(w)))
+    return (q, s, qT, sT) if transposed else (q, s)
+
+
+def fp8_quant_act_128x1_T(x):
+    """x[M][C] -> (qT uint8 [C][M], sT float32 [M/128][C]); M a multiple of 128."""
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D")
+    M, C = x.shape
+    px = _dev(x, "x", (torch.float32, torch.bfloat16))
+    qT = torch.empty((C, M), dtype=torch.uint8, device=x.device)
+    sT = torch.empty((M // 128, C), dtype=torch.float32, device=x.device)
+    _check("fp8_quant_act_128x1_T",
+           lib().fp8_quant_act_128x1_T(px, _in_dtype(x), M, C, qT.data_ptr(), sT.data_ptr(), _stream(x)))
+    return qT, sT
+
+
+def fp8_gemm_blockscaled(A, sA, B, sB, b_scale_mode=SCALE_BLOCK128, out=None):
+    """C[M][N] (bf16) = block-scaled FP8 GEMM of A[M][K] and B[N][K] (both K-contiguous)."""
+    M, K = A.shape
+    N = B.shape[0]
+    if B.shape[1] != K:
+        raise ValueError("A and B disagree on K")
+    if b_scale_mode == SCALE_BLOCK128:
+        exp_sb = (N // 128, K // 128)
+    elif b_scale_mode == SCALE_ROW:
+        exp_sb = (K // 128, N)
+    else:
+        raise ValueError("unknown b_scale_mode")
+    if tuple(sA.shape) != (K // 128, M) or tuple(sB.shape) != exp_sb:
+        raise ValueError(f"scale grids {tuple(sA.shape)}, {tuple(sB.shape)} do not match the operands")
+    pa = _dev(A, "A", (torch.uint8,))
+    psa = _dev(sA, "sA", (torch.float32,))
+    pb = _dev(B, "B", (torch.uint8,))
+    psb = _dev(sB, "sB", (torch.float32,))
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
+    pc = _dev(out, "out", (torch.bfloat16,))
+    if tuple(out.shape) != (M, N):
+        raise ValueError("out has the wrong shape")
+    _check("fp8_gemm_blockscaled",
+           lib().fp8_gemm_blockscaled(pa, psa, pb, psb, int(b_scale_mode), pc, M, N, K, _stream(A)))
+    return out
+
+
+def fp8_grouped_gemm_blockscaled(A, sA, B, sB, group_offsets, out=None):
+    """Per-expert GEMM: rows [off[e], off[e+1]) of A times B[e]; offsets int32 on the GPU."""
+    M_total, K = A.shape
+    E, N, Kb = B.shape
+    if Kb != K:
+        raise ValueError("A and B disagree on K")
+    if tuple(sA.shape) != (K // 128, M_total) or tuple(sB.shape) != (E, N // 128, K // 128):
+        raise ValueError("scale grids do not match the operands")
+    if tuple(group_offsets.shape) != (E + 1,):
+        raise ValueError("group_offsets must have E+1 entries")
+    pa = _dev(A, "A", (torch.uint8,))
+    psa = _dev(sA, "sA", (torch.float32,))
+    pb = _dev(B, "B", (torch.uint8,))
+    psb = _dev(sB, "sB", (torch.float32,))
+    po = _dev(group_offsets, "group_offsets", (torch.int32,))
+    if out is None:
+        out = torch.empty((M_total, N), dtype=torch.bfloat16, device=A.device)
+    pc = _dev(out, "out", (torch.bfloat16,))
+    _check("fp8_grouped_gemm_blockscaled",
+           lib().fp8_grouped_gemm_blockscaled(pa, psa, pb, psb, pc, po, E, M_total, N, K, _stream(A)))
+    return out

@@ -1,0 +1,111 @@
+// C ABI of libfp8bs: host-side argument validation, then one launch on the
+// caller's stream. Declarations and the meaning of every argument are in
+// include/fp8bs.h.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fp8bs.h"
+#include "internal.h"
+
+namespace {
+
+constexpr int64_t kG = 128;
+constexpr int64_t kI32 = (int64_t)1 << 31;
+
+bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+int status_of(hipError_t e) { return e == hipSuccess ? FP8BS_OK : FP8BS_ERR_LAUNCH; }
+
+bool valid_dtype(int d) { return d == FP8BS_F32 || d == FP8BS_BF16; }
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+int fp8bs_abi_version(void) { return FP8BS_ABI_VERSION; }
+
+const char* fp8bs_status_string(int status) {
+  switch (status) {
+    case FP8BS_OK: return "ok";
+    case FP8BS_ERR_NULL_PTR: return "null pointer";
+    case FP8BS_ERR_SHAPE: return "invalid shape (negative, or not a multiple of 128 where required)";
+    case FP8BS_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case FP8BS_ERR_DTYPE: return "unknown input dtype";
+    case FP8BS_ERR_MODE: return "unknown scale mode, or transposed outputs given one-sided";
+    case FP8BS_ERR_LAUNCH: return "kernel launch failed";
+    case FP8BS_ERR_TOO_LARGE: return "size exceeds the supported 32-bit index range";
+    default: return "unknown status";
+  }
+}
+
+int fp8_quant_act_1x128(const void* x, int dtype, int64_t M, int64_t K, uint8_t* q, float* s,
+                        void* stream) {
+  if (!valid_dtype(dtype)) return FP8BS_ERR_DTYPE;
+  if (M < 0 || K < 0 || K % kG) return FP8BS_ERR_SHAPE;
+  if (K >= kI32 || (M > 0 && K > 0 && ((M + 3) / 4) * (K / kG) >= kI32)) return FP8BS_ERR_TOO_LARGE;
+  if (M == 0 || K == 0) return FP8BS_OK;
+  if (!x || !q || !s) return FP8BS_ERR_NULL_PTR;
+  if (misaligned(x) || misaligned(q) || misaligned(s)) return FP8BS_ERR_ALIGN;
+  return status_of(fp8bs::launch_quant_act_1x128(x, dtype == FP8BS_BF16, M, K, q, s, as_stream(stream)));
+}
+
+int fp8_quant_w_128x128(const void* w, int dtype, int64_t N, int64_t K, uint8_t* q, float* s,
+                        uint8_t* qT, float* sT, void* stream) {
+  if (!valid_dtype(dtype)) return FP8BS_ERR_DTYPE;
+  if ((qT == nullptr) != (sT == nullptr)) return FP8BS_ERR_MODE;
+  if (N < 0 || K < 0 || N % kG || K % kG) return FP8BS_ERR_SHAPE;
+  if (N >= kI32 || K >= kI32 || N * K >= kI32 * 4) return FP8BS_ERR_TOO_LARGE;
+  if (N == 0 || K == 0) return FP8BS_OK;
+  if (!w || !q || !s) return FP8BS_ERR_NULL_PTR;
+  if (misaligned(w) || misaligned(q) || misaligned(s) || misaligned(qT) || misaligned(sT))
+    return FP8BS_ERR_ALIGN;
+  if (K / kG > 65535 * 1024 || N / kG > 65535) return FP8BS_ERR_TOO_LARGE;
+  return status_of(fp8bs::launch_quant_w_128x128(w, dtype == FP8BS_BF16, N, K, q, s, qT, sT,
+                                                 as_stream(stream)));
+}
+
+int fp8_quant_act_128x1_T(const void* x, int dtype, int64_t M, int64_t C, uint8_t* qT, float* sT,
+                          void* stream) {
+  if (!valid_dtype(dtype)) return FP8BS_ERR_DTYPE;
+  if (M < 0 || C < 0 || M % kG) return FP8BS_ERR_SHAPE;
+  if (M >= kI32 || C >= kI32 || M / kG > 65535) return FP8BS_ERR_TOO_LARGE;
+  if (M == 0 || C == 0) return FP8BS_OK;
+  if (!x || !qT || !sT) return FP8BS_ERR_NULL_PTR;
+  if (misaligned(x) || misaligned(qT) || misaligned(sT)) return FP8BS_ERR_ALIGN;
+  return status_of(fp8bs::launch_quant_act_128x1_T(x, dtype == FP8BS_BF16, M, C, qT, sT,
+                                                   as_stream(stream)));
+}
+
+int fp8_gemm_blockscaled(const uint8_t* A, const float* sA, const uint8_t* B, const float* sB,
+                         int b_scale_mode, uint16_t* C, int64_t M, int64_t N, int64_t K,
+                         void* stream) {
+  if (b_scale_mode != FP8BS_SCALE_BLOCK128 && b_scale_mode != FP8BS_SCALE_ROW) return FP8BS_ERR_MODE;
+  if (M < 0 || N < 0 || K <= 0 || K % kG || N % kG) return FP8BS_ERR_SHAPE;
+  if (M * K >= kI32 || N * K >= kI32 || M * N >= kI32) return FP8BS_ERR_TOO_LARGE;
+  if (M == 0 || N == 0) return FP8BS_OK;
+  if (!A || !sA || !B || !sB || !C) return FP8BS_ERR_NULL_PTR;
+  if (misaligned(A) || misaligned(sA) || misaligned(B) || misaligned(sB) || misaligned(C))
+    return FP8BS_ERR_ALIGN;
+  return status_of(fp8bs::launch_gemm_blockscaled(A, sA, B, sB, b_scale_mode, C, M, N, K,
+                                                  as_stream(stream)));
+}
+
+int fp8_grouped_gemm_blockscaled(const uint8_t* A, const float* sA, const uint8_t* B,
+                                 const float* sB, uint16_t* C, const int32_t* group_offsets, int E,
+                                 int64_t M_total, int64_t N, int64_t K, void* stream) {
+  if (E < 0 || M_total < 0 || N < 0 || K <= 0 || K % kG || N % kG) return FP8BS_ERR_SHAPE;
+  if (M_total * K >= kI32 || M_total * N >= kI32 || N * K >= kI32 || (int64_t)E * N * K >= kI32 * 4)
+    return FP8BS_ERR_TOO_LARGE;
+  if (E == 0 && M_total > 0) return FP8BS_ERR_SHAPE;   // rows with no expert
+  if (M_total == 0 || N == 0) return FP8BS_OK;
+  if (!A || !sA || !B || !sB || !C || !group_offsets) return FP8BS_ERR_NULL_PTR;
+  if (misaligned(A) || misaligned(sA) || misaligned(B) || misaligned(sB) || misaligned(C))
+    return FP8BS_ERR_ALIGN;
+  return status_of(fp8bs::launch_grouped_gemm_blockscaled(A, sA, B, sB, C, group_offsets, E,
+                                                          M_total, N, K, as_stream(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,24 @@
+// Launchers behind the C ABI of libfp8bs (shapes and pointers are validated by
+// the ABI layer before any of these is called).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8bs {
+
+hipError_t launch_quant_act_1x128(const void* x, bool bf16, int64_t M, int64_t K, uint8_t* q,
+                                  float* s, hipStream_t stream);
+hipError_t launch_quant_w_128x128(const void* w, bool bf16, int64_t N, int64_t K, uint8_t* q,
+                                  float* s, uint8_t* qT, float* sT, hipStream_t stream);
+hipError_t launch_quant_act_128x1_T(const void* x, bool bf16, int64_t M, int64_t C, uint8_t* qT,
+                                    float* sT, hipStream_t stream);
+hipError_t launch_gemm_blockscaled(const uint8_t* A, const float* sA, const uint8_t* B,
+                                   const float* sB, int row_mode, uint16_t* C, int64_t M,
+                                   int64_t N, int64_t K, hipStream_t stream);
+hipError_t launch_grouped_gemm_blockscaled(const uint8_t* A, const float* sA, const uint8_t* B,
+                                           const float* sB, uint16_t* C, const int32_t* offsets,
+                                           int E, int64_t M_total, int64_t N, int64_t K,
+                                           hipStream_t stream);
+
+}  // namespace fp8bs

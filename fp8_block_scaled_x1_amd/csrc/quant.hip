@@ -1,0 +1,311 @@
+// Fine-grained E4M3 quantizers for gfx950 (memory-bound; one pass over the
+// input, amax reduction and cast fused).
+//
+// The method: DeepSeek-V3 report section 3.3.2, as paraphrased on the
+// innerforce.co.kr page -- elements are quantized in small groups that share a
+// scaling factor, with the groups laid along the GEMM's inner dimension, and
+// E4M3 is used for every tensor. The pages wish for the FP8 conversion to be
+// fused with the data movement itself (report section 3.5.2); on gfx950 the
+// equivalent is a single streaming kernel that reads each element once from
+// HBM, reduces amax in registers (DPP) and writes codes and scales.
+//
+// Group geometry (a reading; the pages only say "small groups"):
+//   quant_act_1x128   one row x 128 consecutive K           s[K/128][M]
+//   quant_w_128x128   128 x 128 block                        s[N/128][K/128]
+//   quant_act_128x1_T 128 consecutive tokens of one channel, written
+//                     transposed (the pages call a transposition fused into
+//                     the GEMM cumbersome, report section 3.5.2)  sT[M/128][C]
+
+#include "device_common.h"
+#include "internal.h"
+
+namespace fp8bs {
+
+// ---------------------------------------------------------------------------
+// Loads of 8 consecutive high-precision elements as FP32 (exact widening).
+// ---------------------------------------------------------------------------
+template <bool BF16>
+__device__ __forceinline__ void load8(const void* base, int64_t elem, float v[8]) {
+  if constexpr (BF16) {
+    const uint4 d = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(base) + elem);
+    const uint32_t w[4] = {d.x, d.y, d.z, d.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  } else {
+    const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + elem);
+    const float4 a = p[0], b = p[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+}
+
+__device__ __forceinline__ uint2 cast8(const float v[8], float s) {
+  uint32_t c[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) c[i] = e4m3_code(v[i] / s);
+  return make_uint2(pack4(c[0], c[1], c[2], c[3]), pack4(c[4], c[5], c[6], c[7]));
+}
+
+// ---------------------------------------------------------------------------
+// 1x128 activation quantizer.
+// A wave handles 4 groups at once: rows 4*mq .. 4*mq+3 of one K chunk kb.
+// Lane l: row 4*mq + l/16, elements kb*128 + (l%16)*8 .. +7. The 16 lanes of a
+// DPP row form one group, so amax is a 4-step row rotation. Each wave does
+// kUnroll consecutive chunks of the same rows to keep loads in flight.
+// ---------------------------------------------------------------------------
+constexpr int kActUnroll = 2;
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void quant_act_1x128_kernel(
+    const void* __restrict__ x, int64_t M, int K, uint8_t* __restrict__ q,
+    float* __restrict__ s, uint32_t wave_tasks) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const uint32_t nkb = (uint32_t)K / kGroup;
+  const int part = lane & 15;
+  const uint32_t wt0 = (blockIdx.x * 4u + wave) * kActUnroll;
+
+  float v[kActUnroll][8];
+  int64_t row[kActUnroll];
+  uint32_t kb[kActUnroll];
+  bool live[kActUnroll];
+#pragma unroll
+  for (int u = 0; u < kActUnroll; ++u) {
+    const uint32_t wt = wt0 + u;
+    const uint32_t mq = wt / nkb;
+    kb[u] = wt - mq * nkb;
+    row[u] = (int64_t)mq * 4 + (lane >> 4);
+    live[u] = wt < wave_tasks && row[u] < M;
+    if (live[u]) {
+      load8<BF16>(x, row[u] * K + kb[u] * kGroup + part * 8, v[u]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[u][i] = 0.0f;
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kActUnroll; ++u) {
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[u][i]));
+    amax = row16_max(amax);
+    const float sc = group_scale(amax);
+    const uint2 codes = cast8(v[u], sc);
+    if (live[u]) {
+      *reinterpret_cast<uint2*>(q + row[u] * K + kb[u] * kGroup + part * 8) = codes;
+      if (part == 0) s[(int64_t)kb[u] * M + row[u]] = sc;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 128x128 weight quantizer: one workgroup (256 threads) per block (nb, kb).
+// Thread t covers rows i*16 + t/16 (i = 0..7), elements (t%16)*8 .. +7 of the
+// block: 8 independent 16-byte loads in flight, 64 values in registers.
+// With a transposed copy requested, the codes also go through an LDS tile and
+// leave as 4x4-byte transposed pieces so that qT rows are written coalesced.
+// ---------------------------------------------------------------------------
+constexpr int kTileStride = kGroup + 4;   // LDS row pitch in bytes (padding against bank conflicts)
+
+template <bool BF16, bool TRANS>
+__global__ __launch_bounds__(256) void quant_w_128x128_kernel(
+    const void* __restrict__ w, int N, int K, uint8_t* __restrict__ q, float* __restrict__ s,
+    uint8_t* __restrict__ qT, float* __restrict__ sT) {
+  __shared__ float red[4];
+  __shared__ __align__(16) uint8_t tile[TRANS ? kGroup * kTileStride : 4];
+  const int t = threadIdx.x;
+  const int kb = blockIdx.x, nb = blockIdx.y;
+  const int nkb = K / kGroup, nnb = N / kGroup;
+  const int r0 = t >> 4, part = t & 15;
+
+  float v[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int64_t row = (int64_t)nb * kGroup + i * 16 + r0;
+    load8<BF16>(w, row * K + (int64_t)kb * kGroup + part * 8, v[i]);
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[i][j]));
+  amax = wave_max(amax);
+  if ((t & 63) == 0) red[t >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float sc = group_scale(amax);
+
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int rl = i * 16 + r0;
+    const uint2 codes = cast8(v[i], sc);
+    *reinterpret_cast<uint2*>(q + ((int64_t)nb * kGroup + rl) * K + (int64_t)kb * kGroup + part * 8) = codes;
+    if constexpr (TRANS) {
+      uint32_t* d = reinterpret_cast<uint32_t*>(tile + rl * kTileStride + part * 8);
+      d[0] = codes.x;
+      d[1] = codes.y;
+    }
+  }
+  if (t == 0) {
+    s[nb * nkb + kb] = sc;
+    if constexpr (TRANS) sT[kb * nnb + nb] = sc;
+  }
+  if constexpr (TRANS) {
+    __syncthreads();
+    // 32x32 pieces of 4x4 bytes; piece (pr, pc) covers tile rows 4pr..4pr+3,
+    // columns 4pc..4pc+3 and lands in qT rows kb*128 + 4pc + j, columns
+    // nb*128 + 4pr .. +3.
+#pragma unroll
+    for (int j4 = 0; j4 < 4; ++j4) {
+      const int piece = t + 256 * j4;
+      const int pr = piece & 31, pc = piece >> 5;
+      uint32_t d[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        d[i] = *reinterpret_cast<const uint32_t*>(tile + (4 * pr + i) * kTileStride + 4 * pc);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t out = ((d[0] >> (8 * j)) & 0xFFu) | (((d[1] >> (8 * j)) & 0xFFu) << 8) |
+                             (((d[2] >> (8 * j)) & 0xFFu) << 16) | (((d[3] >> (8 * j)) & 0xFFu) << 24);
+        *reinterpret_cast<uint32_t*>(qT + ((int64_t)kb * kGroup + 4 * pc + j) * N +
+                                     (int64_t)nb * kGroup + 4 * pr) = out;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 128x1 transposed quantizer: one workgroup per (token chunk tb, 64 channels).
+// Thread t: channel pair cp = t%32 (channels c0+2cp, c0+2cp+1), token slice
+// tg = t/32 (tokens 16tg .. 16tg+15 of the chunk). Loads of consecutive lanes
+// cover 128 contiguous bytes of an input row (BF16). Per-channel amax is
+// combined across the 8 token slices through LDS; each thread then writes its
+// 16 codes per channel as one 16-byte piece of a qT row.
+// ---------------------------------------------------------------------------
+template <bool BF16, bool PAIR>
+__global__ __launch_bounds__(256) void quant_act_128x1_T_kernel(
+    const void* __restrict__ x, int64_t M, int C, uint8_t* __restrict__ qT, float* __restrict__ sT) {
+  __shared__ float red[8][64];
+  __shared__ float scl[64];
+  const int t = threadIdx.x;
+  const int cp = t & 31, tg = t >> 5;
+  const int tb = blockIdx.y;
+  const int c0 = blockIdx.x * 64;
+  const int ch = c0 + 2 * cp;
+  const bool ok0 = ch < C, ok1 = ch + 1 < C;
+  const int64_t tok0 = (int64_t)tb * kGroup + tg * 16;
+
+  float v0[16], v1[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int64_t e = (tok0 + i) * C + ch;
+    if constexpr (PAIR) {
+      if (ok0) {   // C even: ch < C implies ch + 1 < C
+        if constexpr (BF16) {
+          const uint32_t d = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint16_t*>(x) + e);
+          v0[i] = __uint_as_float(d << 16);
+          v1[i] = __uint_as_float(d & 0xFFFF0000u);
+        } else {
+          const float2 d = *reinterpret_cast<const float2*>(reinterpret_cast<const float*>(x) + e);
+          v0[i] = d.x;
+          v1[i] = d.y;
+        }
+      } else {
+        v0[i] = 0.0f;
+        v1[i] = 0.0f;
+      }
+    } else {
+      if constexpr (BF16) {
+        const uint16_t* xb = reinterpret_cast<const uint16_t*>(x);
+        v0[i] = ok0 ? bf16_bits_to_float(xb[e]) : 0.0f;
+        v1[i] = ok1 ? bf16_bits_to_float(xb[e + 1]) : 0.0f;
+      } else {
+        const float* xf = reinterpret_cast<const float*>(x);
+        v0[i] = ok0 ? xf[e] : 0.0f;
+        v1[i] = ok1 ? xf[e + 1] : 0.0f;
+      }
+    }
+  }
+  float a0 = 0.0f, a1 = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    a0 = fmaxf(a0, fabsf(v0[i]));
+    a1 = fmaxf(a1, fabsf(v1[i]));
+  }
+  red[tg][2 * cp] = a0;
+  red[tg][2 * cp + 1] = a1;
+  __syncthreads();
+  if (t < 64) {
+    float amax = red[0][t];
+#pragma unroll
+    for (int g = 1; g < 8; ++g) amax = fmaxf(amax, red[g][t]);
+    const float sc = group_scale(amax);
+    scl[t] = sc;
+    if (c0 + t < C) sT[(int64_t)tb * C + c0 + t] = sc;
+  }
+  __syncthreads();
+  const float s0 = scl[2 * cp], s1 = scl[2 * cp + 1];
+  uint32_t w0[4], w1[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    w0[j] = pack4(e4m3_code(v0[4 * j] / s0), e4m3_code(v0[4 * j + 1] / s0),
+                  e4m3_code(v0[4 * j + 2] / s0), e4m3_code(v0[4 * j + 3] / s0));
+    w1[j] = pack4(e4m3_code(v1[4 * j] / s1), e4m3_code(v1[4 * j + 1] / s1),
+                  e4m3_code(v1[4 * j + 2] / s1), e4m3_code(v1[4 * j + 3] / s1));
+  }
+  if (ok0) *reinterpret_cast<uint4*>(qT + (int64_t)ch * M + tok0) = make_uint4(w0[0], w0[1], w0[2], w0[3]);
+  if (ok1) *reinterpret_cast<uint4*>(qT + (int64_t)(ch + 1) * M + tok0) = make_uint4(w1[0], w1[1], w1[2], w1[3]);
+}
+
+// ---------------------------------------------------------------------------
+// Launchers (shapes validated by the C ABI layer).
+// ---------------------------------------------------------------------------
+hipError_t launch_quant_act_1x128(const void* x, bool bf16, int64_t M, int64_t K, uint8_t* q,
+                                  float* s, hipStream_t stream) {
+  const uint32_t nkb = (uint32_t)(K / kGroup);
+  const uint32_t wave_tasks = (uint32_t)((M + 3) / 4) * nkb;
+  const uint32_t per_block = 4 * kActUnroll;
+  const uint32_t blocks = (wave_tasks + per_block - 1) / per_block;
+  if (bf16)
+    hipLaunchKernelGGL(quant_act_1x128_kernel<true>, dim3(blocks), dim3(256), 0, stream, x, M,
+                       (int)K, q, s, wave_tasks);
+  else
+    hipLaunchKernelGGL(quant_act_1x128_kernel<false>, dim3(blocks), dim3(256), 0, stream, x, M,
+                       (int)K, q, s, wave_tasks);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_w_128x128(const void* w, bool bf16, int64_t N, int64_t K, uint8_t* q,
+                                  float* s, uint8_t* qT, float* sT, hipStream_t stream) {
+  const dim3 grid((unsigned)(K / kGroup), (unsigned)(N / kGroup));
+  const bool tr = qT != nullptr;
+  if (bf16 && tr)
+    hipLaunchKernelGGL((quant_w_128x128_kernel<true, true>), grid, dim3(256), 0, stream, w, (int)N, (int)K, q, s, qT, sT);
+  else if (bf16)
+    hipLaunchKernelGGL((quant_w_128x128_kernel<true, false>), grid, dim3(256), 0, stream, w, (int)N, (int)K, q, s, qT, sT);
+  else if (tr)
+    hipLaunchKernelGGL((quant_w_128x128_kernel<false, true>), grid, dim3(256), 0, stream, w, (int)N, (int)K, q, s, qT, sT);
+  else
+    hipLaunchKernelGGL((quant_w_128x128_kernel<false, false>), grid, dim3(256), 0, stream, w, (int)N, (int)K, q, s, qT, sT);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_act_128x1_T(const void* x, bool bf16, int64_t M, int64_t C, uint8_t* qT,
+                                    float* sT, hipStream_t stream) {
+  const dim3 grid((unsigned)((C + 63) / 64), (unsigned)(M / kGroup));
+  const bool pair = (C % 2) == 0;
+  if (bf16 && pair)
+    hipLaunchKernelGGL((quant_act_128x1_T_kernel<true, true>), grid, dim3(256), 0, stream, x, M, (int)C, qT, sT);
+  else if (bf16)
+    hipLaunchKernelGGL((quant_act_128x1_T_kernel<true, false>), grid, dim3(256), 0, stream, x, M, (int)C, qT, sT);
+  else if (pair)
+    hipLaunchKernelGGL((quant_act_128x1_T_kernel<false, true>), grid, dim3(256), 0, stream, x, M, (int)C, qT, sT);
+  else
+    hipLaunchKernelGGL((quant_act_128x1_T_kernel<false, false>), grid, dim3(256), 0, stream, x, M, (int)C, qT, sT);
+  return hipGetLastError();
+}
+
+}  // namespace fp8bs

@@ -47,6 +47,10 @@ extern "C" {
 
 #define FP8BS_ABI_VERSION 1
 
+#ifndef FP8BS_API
+#define FP8BS_API __attribute__((visibility("default")))
+#endif
+
 /* High-precision input type of the quantizers. */
 enum fp8bs_dtype { FP8BS_F32 = 0, FP8BS_BF16 = 1 };
 
@@ -72,7 +76,7 @@ enum fp8bs_status {
  *   s  [K/128][M]  float32, s[kb][m] = amax(group)/448, 1.0 for a zero group
  * K must be a multiple of 128; any M >= 0 (M == 0 or K == 0: no-op).
  */
-int fp8_quant_act_1x128(const void* x, int dtype, int64_t M, int64_t K,
+FP8BS_API int fp8_quant_act_1x128(const void* x, int dtype, int64_t M, int64_t K,
                         uint8_t* q, float* s, void* stream);
 
 /*
@@ -87,7 +91,7 @@ int fp8_quant_act_1x128(const void* x, int dtype, int64_t M, int64_t K,
  *   sT  [K/128][N/128]   float32, sT = s^T      (NULL: not written)
  * qT and sT must be both given or both NULL. N and K multiples of 128.
  */
-int fp8_quant_w_128x128(const void* w, int dtype, int64_t N, int64_t K,
+FP8BS_API int fp8_quant_w_128x128(const void* w, int dtype, int64_t N, int64_t K,
                         uint8_t* q, float* s, uint8_t* qT, float* sT,
                         void* stream);
 
@@ -102,7 +106,7 @@ int fp8_quant_w_128x128(const void* w, int dtype, int64_t N, int64_t K,
  *   sT  [M/128][C]   float32
  * M must be a multiple of 128; any C >= 0.
  */
-int fp8_quant_act_128x1_T(const void* x, int dtype, int64_t M, int64_t C,
+FP8BS_API int fp8_quant_act_128x1_T(const void* x, int dtype, int64_t M, int64_t C,
                           uint8_t* qT, float* sT, void* stream);
 
 /*
@@ -120,7 +124,7 @@ int fp8_quant_act_128x1_T(const void* x, int dtype, int64_t M, int64_t C,
  *   C   [M][N]  BF16 bits, round to nearest even
  * K and N multiples of 128; any M >= 0. M*K, N*K and M*N below 2^31.
  */
-int fp8_gemm_blockscaled(const uint8_t* A, const float* sA, const uint8_t* B,
+FP8BS_API int fp8_gemm_blockscaled(const uint8_t* A, const float* sA, const uint8_t* B,
                          const float* sB, int b_scale_mode, uint16_t* C,
                          int64_t M, int64_t N, int64_t K, void* stream);
 
@@ -137,17 +141,17 @@ int fp8_gemm_blockscaled(const uint8_t* A, const float* sA, const uint8_t* B,
  *                  the kernels clamp every row index into [0, M_total)).
  * K and N multiples of 128; E >= 0; M_total >= 0.
  */
-int fp8_grouped_gemm_blockscaled(const uint8_t* A, const float* sA,
+FP8BS_API int fp8_grouped_gemm_blockscaled(const uint8_t* A, const float* sA,
                                  const uint8_t* B, const float* sB,
                                  uint16_t* C, const int32_t* group_offsets,
                                  int E, int64_t M_total, int64_t N, int64_t K,
                                  void* stream);
 
 /* Human-readable name of a status code (static string). */
-const char* fp8bs_status_string(int status);
+FP8BS_API const char* fp8bs_status_string(int status);
 
 /* FP8BS_ABI_VERSION of the loaded library. */
-int fp8bs_abi_version(void);
+FP8BS_API int fp8bs_abi_version(void);
 
 #ifdef __cplusplus
 }

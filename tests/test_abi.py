@@ -1,0 +1,116 @@
+"""The C ABI library loads, exports every entry point its header declares, and
+rejects invalid arguments on the host, before anything touches a device.
+
+Runs without a GPU: every call below fails validation, so no HIP API call is
+made.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8bs.h")
+
+import fp8_block_scaled_x1_amd as fb  # noqa: E402
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    return re.findall(r"FP8BS_API\s+[\w\s\*]+?\b(\w+)\s*\(", text)
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(fb.LIB_PATH):
+        pytest.skip("libfp8bs.so not built")
+    return fb.lib()
+
+
+def test_header_declares_the_five_entry_points():
+    names = set(_declared_functions())
+    assert {"fp8_quant_act_1x128", "fp8_quant_w_128x128", "fp8_quant_act_128x1_T",
+            "fp8_gemm_blockscaled", "fp8_grouped_gemm_blockscaled",
+            "fp8bs_status_string", "fp8bs_abi_version"} == names
+
+
+def test_library_exports_every_declared_symbol(L):
+    raw = ctypes.CDLL(fb.LIB_PATH)
+    for name in _declared_functions():
+        assert hasattr(raw, name), name
+
+
+def test_version_and_status_strings(L):
+    assert L.fp8bs_abi_version() == fb.ABI_VERSION == 1
+    for code in range(-7, 1):
+        assert fb.status_string(code) not in ("", "unknown status")
+    assert fb.status_string(-99) == "unknown status"
+
+
+NULL = None
+P = 4096   # a fake, 16-byte aligned, non-null address: never dereferenced by a failing call
+MIS = 4100
+
+
+def test_quant_act_validation(L):
+    f = L.fp8_quant_act_1x128
+    assert f(P, 2, 4, 128, P, P, NULL) == -4          # dtype
+    assert f(P, 1, 4, 100, P, P, NULL) == -2          # K not a multiple of 128
+    assert f(P, 1, -1, 128, P, P, NULL) == -2
+    assert f(NULL, 1, 4, 128, P, P, NULL) == -1
+    assert f(P, 1, 4, 128, NULL, P, NULL) == -1
+    assert f(MIS, 1, 4, 128, P, P, NULL) == -3
+    assert f(P, 1, 4, 128, P, MIS, NULL) == -3
+    assert f(NULL, 1, 0, 128, NULL, NULL, NULL) == 0  # empty: no-op
+    assert f(NULL, 0, 7, 0, NULL, NULL, NULL) == 0
+
+
+def test_quant_w_validation(L):
+    f = L.fp8_quant_w_128x128
+    assert f(P, 1, 128, 128, P, P, P, NULL, NULL) == -5   # one-sided transposed outputs
+    assert f(P, 1, 100, 128, P, P, NULL, NULL, NULL) == -2
+    assert f(P, 1, 128, 200, P, P, NULL, NULL, NULL) == -2
+    assert f(P, 5, 128, 128, P, P, NULL, NULL, NULL) == -4
+    assert f(NULL, 1, 128, 128, P, P, NULL, NULL, NULL) == -1
+    assert f(P, 1, 128, 128, P, P, MIS, P, NULL) == -3
+    assert f(NULL, 1, 0, 128, NULL, NULL, NULL, NULL, NULL) == 0
+
+
+def test_quant_128x1_validation(L):
+    f = L.fp8_quant_act_128x1_T
+    assert f(P, 1, 100, 64, P, P, NULL) == -2         # M not a multiple of 128
+    assert f(P, 1, 128, -3, P, P, NULL) == -2
+    assert f(P, 1, 128, 64, NULL, P, NULL) == -1
+    assert f(P, 1, 128, 64, P, MIS, NULL) == -3
+    assert f(NULL, 1, 128, 0, NULL, NULL, NULL) == 0
+
+
+def test_gemm_validation(L):
+    f = L.fp8_gemm_blockscaled
+    assert f(P, P, P, P, 2, P, 4, 128, 128, NULL) == -5
+    assert f(P, P, P, P, 0, P, 4, 100, 128, NULL) == -2   # N not a multiple of 128
+    assert f(P, P, P, P, 0, P, 4, 128, 0, NULL) == -2     # K must be positive
+    assert f(P, P, P, P, 0, P, 4, 128, 130, NULL) == -2
+    assert f(P, P, NULL, P, 0, P, 4, 128, 128, NULL) == -1
+    assert f(P, P, P, P, 0, MIS, 4, 128, 128, NULL) == -3
+    assert f(P, P, P, P, 0, P, 1 << 20, 1 << 12, 1 << 12, NULL) == -7   # M*N >= 2^31
+    assert f(NULL, NULL, NULL, NULL, 1, NULL, 0, 128, 128, NULL) == 0  # M == 0: no-op
+
+
+def test_grouped_validation(L):
+    f = L.fp8_grouped_gemm_blockscaled
+    assert f(P, P, P, P, P, P, -1, 4, 128, 128, NULL) == -2
+    assert f(P, P, P, P, P, P, 0, 4, 128, 128, NULL) == -2      # rows but no experts
+    assert f(P, P, P, P, P, NULL, 2, 4, 128, 128, NULL) == -1   # offsets missing
+    assert f(P, P, P, P, P, P, 2, 4, 128, 100, NULL) == -2
+    assert f(MIS, P, P, P, P, P, 2, 4, 128, 128, NULL) == -3
+    assert f(NULL, NULL, NULL, NULL, NULL, NULL, 3, 0, 128, 128, NULL) == 0
+
+
+def test_binding_requires_gpu_tensors(L):
+    import torch
+    x = torch.zeros(4, 128)
+    with pytest.raises(ValueError):
+        fb.fp8_quant_act_1x128(x)
