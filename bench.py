@@ -1,0 +1,424 @@
+#!/usr/bin/env python3
+"""Throughput of the fine-grained FP8 block-scaled GEMM path on one MI355X.
+
+One step is one pass of the path over one batch of synthetic input. The
+default workload is the dense Fprop projection (X[4096][7168] BF16 quantized
+1x128, W[7168][7168] BF16 quantized 128x128, block-scaled FP8 GEMM with FP32
+promotion per 128-wide K chunk, BF16 output). Other workloads (--workload)
+measure the remaining forms of the path: the backward pair (Dgrad + Wgrad with
+the 128x1 transposed quantizer), the grouped MoE expert GEMMs and the
+decode-shaped grouped GEMM.
+
+Prints one JSON line. `value` is whole-step throughput with inputs resident in
+HBM; `roofline` describes the dominant kernel, timed live with HIP events on
+the stream the kernels run on; `cpu_baseline` times the CPU oracle on a
+bounded sample of the same step (rank 0, one GPU only).
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "FP8 block-scaled GEMM TFLOPS and % of MI355X FP8 MFMA peak; quant GB/s"
+PEAK_FP8_TFLOPS = 5000.0     # MI355X dense FP8 MFMA (published)
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E (published)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "fp8_block_scaled_x1_amd", "csrc", f)
+                  for f in ("gemm.hip", "quant.hip", "device_common.h")]
+
+
+def kernel_source_digest():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from committed rocprofv3 counters, if still current."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = t.get(f"{workload}:{kernel}")
+    if not ent or ent.get("source_digest") != kernel_source_digest():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+class Timer:
+    """HIP events around each kernel of a step, on the current stream."""
+
+    def __init__(self, torch, names, steps):
+        self.torch = torch
+        self.names = names
+        self.ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(steps)]
+        self.i = 0
+        self.k = 0
+
+    def mark(self):
+        if self.i < len(self.ev):
+            self.ev[self.i][self.k].record()
+        self.k += 1
+        if self.k == len(self.names) + 1:
+            self.k = 0
+            self.i += 1
+
+    def averages_us(self):
+        out = {}
+        for j, n in enumerate(self.names):
+            ts = [row[j].elapsed_time(row[j + 1]) * 1e3 for row in self.ev[:self.i]]
+            out[n] = sum(ts) / len(ts)
+        return out
+
+
+# ---------------------------------------------------------------------------
+# workloads: each returns (step(timer), info dict)
+# ---------------------------------------------------------------------------
+
+def _rotations(bytes_per_set, target=600e6):
+    """Copies of the inputs to cycle through so the working set exceeds the 256 MB
+    Infinity Cache (the inputs are then served from HBM, not from the cache)."""
+    return max(2, int(-(-target // bytes_per_set)))
+
+
+def setup_dense_fprop(torch, fb, dev, M=4096, N=7168, K=7168):
+    import workloads
+    sets = []
+    R = _rotations(M * K * 2 + N * K * 2 + M * K + N * K + M * N * 2)
+    for r in range(R):
+        d = workloads.dense_fprop(device=dev, seed=r, M=M, N=N, K=K)
+        sets.append({
+            "X": d["X"], "W": d["W"],
+            "qx": torch.empty((M, K), dtype=torch.uint8, device=dev),
+            "sx": torch.empty((K // 128, M), dtype=torch.float32, device=dev),
+            "qw": torch.empty((N, K), dtype=torch.uint8, device=dev),
+            "sw": torch.empty((N // 128, K // 128), dtype=torch.float32, device=dev),
+            "C": torch.empty((M, N), dtype=torch.bfloat16, device=dev),
+        })
+    L = fb.lib()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    state = {"i": 0}
+
+    def step(timer):
+        s = sets[state["i"] % R]
+        state["i"] += 1
+        timer.mark()
+        rc = L.fp8_quant_act_1x128(s["X"].data_ptr(), fb.BF16, M, K, s["qx"].data_ptr(), s["sx"].data_ptr(), stream)
+        timer.mark()
+        rc |= L.fp8_quant_w_128x128(s["W"].data_ptr(), fb.BF16, N, K, s["qw"].data_ptr(), s["sw"].data_ptr(),
+                                    None, None, stream)
+        timer.mark()
+        rc |= L.fp8_gemm_blockscaled(s["qx"].data_ptr(), s["sx"].data_ptr(), s["qw"].data_ptr(),
+                                     s["sw"].data_ptr(), fb.SCALE_BLOCK128, s["C"].data_ptr(), M, N, K, stream)
+        timer.mark()
+        if rc:
+            raise RuntimeError(f"libfp8bs call failed ({rc})")
+
+    flops = 2.0 * M * N * K
+    info = {
+        "names": ["quant_act_1x128", "quant_w_128x128", "gemm_blockscaled"],
+        "step_flops": flops,
+        "work": {
+            "quant_act_1x128": ("GB/s", M * K * 2 + M * K + M * K // 128 * 4),
+            "quant_w_128x128": ("GB/s", N * K * 2 + N * K + N * K // 16384 * 4),
+            "gemm_blockscaled": ("TFLOP/s", flops),
+        },
+        "dominant": "gemm_blockscaled",
+        "config": {"workload": f"dense Fprop projection X[{M}x{K}] bf16 1x128, W[{N}x{K}] bf16 128x128, "
+                               f"C[{M}x{N}] bf16", "M": M, "N": N, "K": K, "input_rotations": R},
+    }
+    return step, info
+
+
+def setup_backward(torch, fb, dev, M=4096, N=7168, K=7168):
+    """Dgrad dX = dY W and Wgrad dW = dY^T X, with the quantizers they need."""
+    import workloads
+    R = _rotations(2 * M * N * 2 + M * K * 2 + N * K * 2)
+    sets = []
+    for r in range(R):
+        d = workloads.backward_pair(device=dev, seed=r, M=M, N=N, K=K)
+        qw, sw, qwT, swT = fb.fp8_quant_w_128x128(d["W"], transposed=True)   # weights: quantized in Fprop
+        sets.append({
+            "dY": d["dY"], "X": d["X"], "qwT": qwT, "swT": swT,
+            "qdy": torch.empty((M, N), dtype=torch.uint8, device=dev),
+            "sdy": torch.empty((N // 128, M), dtype=torch.float32, device=dev),
+            "qdyT": torch.empty((N, M), dtype=torch.uint8, device=dev),
+            "sdyT": torch.empty((M // 128, N), dtype=torch.float32, device=dev),
+            "qxT": torch.empty((K, M), dtype=torch.uint8, device=dev),
+            "sxT": torch.empty((M // 128, K), dtype=torch.float32, device=dev),
+            "dX": torch.empty((M, K), dtype=torch.bfloat16, device=dev),
+            "dW": torch.empty((N, K), dtype=torch.bfloat16, device=dev),
+        })
+        del qw, sw
+    L = fb.lib()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    state = {"i": 0}
+
+    def step(timer):
+        s = sets[state["i"] % R]
+        state["i"] += 1
+        timer.mark()
+        rc = L.fp8_quant_act_1x128(s["dY"].data_ptr(), fb.BF16, M, N, s["qdy"].data_ptr(), s["sdy"].data_ptr(), stream)
+        timer.mark()
+        rc |= L.fp8_quant_act_128x1_T(s["dY"].data_ptr(), fb.BF16, M, N, s["qdyT"].data_ptr(), s["sdyT"].data_ptr(), stream)
+        timer.mark()
+        rc |= L.fp8_quant_act_128x1_T(s["X"].data_ptr(), fb.BF16, M, K, s["qxT"].data_ptr(), s["sxT"].data_ptr(), stream)
+        timer.mark()
+        rc |= L.fp8_gemm_blockscaled(s["qdy"].data_ptr(), s["sdy"].data_ptr(), s["qwT"].data_ptr(), s["swT"].data_ptr(),
+                                     fb.SCALE_BLOCK128, s["dX"].data_ptr(), M, K, N, stream)
+        timer.mark()
+        rc |= L.fp8_gemm_blockscaled(s["qdyT"].data_ptr(), s["sdyT"].data_ptr(), s["qxT"].data_ptr(), s["sxT"].data_ptr(),
+                                     fb.SCALE_ROW, s["dW"].data_ptr(), N, K, M, stream)
+        timer.mark()
+        if rc:
+            raise RuntimeError(f"libfp8bs call failed ({rc})")
+
+    flops = 2.0 * M * N * K
+    qb = M * N * 2 + M * N + M * N // 128 * 4
+    info = {
+        "names": ["quant_act_1x128(dY)", "quant_act_128x1_T(dY)", "quant_act_128x1_T(X)", "gemm_dgrad", "gemm_wgrad"],
+        "step_flops": 2 * flops,
+        "work": {
+            "quant_act_1x128(dY)": ("GB/s", qb),
+            "quant_act_128x1_T(dY)": ("GB/s", qb),
+            "quant_act_128x1_T(X)": ("GB/s", M * K * 2 + M * K + M * K // 128 * 4),
+            "gemm_dgrad": ("TFLOP/s", flops),
+            "gemm_wgrad": ("TFLOP/s", flops),
+        },
+        "dominant": "gemm_wgrad",
+        "config": {"workload": f"backward pair: Dgrad dX[{M}x{K}] = dY[{M}x{N}] W, Wgrad dW[{N}x{K}] = dY^T X "
+                               f"over {M} tokens", "M": M, "N": N, "K": K, "input_rotations": R},
+    }
+    return step, info
+
+
+def _quantized_experts(torch, fb, dev, W):
+    E, N, K = W.shape
+    qw = torch.empty((E, N, K), dtype=torch.uint8, device=dev)
+    sw = torch.empty((E, N // 128, K // 128), dtype=torch.float32, device=dev)
+    for e in range(E):
+        qw[e], sw[e] = fb.fp8_quant_w_128x128(W[e])
+    return qw, sw
+
+
+def setup_moe(torch, fb, dev):
+    """Grouped expert GEMMs: up (K=7168 -> N=4096) then down (K=2048 -> N=7168)."""
+    import workloads
+    d = workloads.grouped_moe(device=dev)
+    off = torch.from_numpy(d["offsets"]).to(dev)
+    Mt = int(d["offsets"][-1])
+    E = len(d["counts"])
+    qwu, swu = _quantized_experts(torch, fb, dev, d.pop("W_up"))
+    qwd, swd = _quantized_experts(torch, fb, dev, d.pop("W_dn"))
+    Nu, Ku = qwu.shape[1:]
+    Nd, Kd = qwd.shape[1:]
+    bufs = {
+        "qa": torch.empty((Mt, Ku), dtype=torch.uint8, device=dev),
+        "sa": torch.empty((Ku // 128, Mt), dtype=torch.float32, device=dev),
+        "qh": torch.empty((Mt, Kd), dtype=torch.uint8, device=dev),
+        "sh": torch.empty((Kd // 128, Mt), dtype=torch.float32, device=dev),
+        "Cu": torch.empty((Mt, Nu), dtype=torch.bfloat16, device=dev),
+        "Cd": torch.empty((Mt, Nd), dtype=torch.bfloat16, device=dev),
+    }
+    L = fb.lib()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    A_up, A_dn = d["A_up"], d["A_dn"]
+
+    def step(timer):
+        b = bufs
+        timer.mark()
+        rc = L.fp8_quant_act_1x128(A_up.data_ptr(), fb.BF16, Mt, Ku, b["qa"].data_ptr(), b["sa"].data_ptr(), stream)
+        timer.mark()
+        rc |= L.fp8_grouped_gemm_blockscaled(b["qa"].data_ptr(), b["sa"].data_ptr(), qwu.data_ptr(), swu.data_ptr(),
+                                             b["Cu"].data_ptr(), off.data_ptr(), E, Mt, Nu, Ku, stream)
+        timer.mark()
+        rc |= L.fp8_quant_act_1x128(A_dn.data_ptr(), fb.BF16, Mt, Kd, b["qh"].data_ptr(), b["sh"].data_ptr(), stream)
+        timer.mark()
+        rc |= L.fp8_grouped_gemm_blockscaled(b["qh"].data_ptr(), b["sh"].data_ptr(), qwd.data_ptr(), swd.data_ptr(),
+                                             b["Cd"].data_ptr(), off.data_ptr(), E, Mt, Nd, Kd, stream)
+        timer.mark()
+        if rc:
+            raise RuntimeError(f"libfp8bs call failed ({rc})")
+
+    fu, fd = 2.0 * Mt * Nu * Ku, 2.0 * Mt * Nd * Kd
+    info = {
+        "names": ["quant_act_1x128(up)", "grouped_gemm_up", "quant_act_1x128(down)", "grouped_gemm_down"],
+        "step_flops": fu + fd,
+        "work": {
+            "quant_act_1x128(up)": ("GB/s", Mt * Ku * 3 + Mt * Ku // 32),
+            "grouped_gemm_up": ("TFLOP/s", fu),
+            "quant_act_1x128(down)": ("GB/s", Mt * Kd * 3 + Mt * Kd // 32),
+            "grouped_gemm_down": ("TFLOP/s", fd),
+        },
+        "dominant": "grouped_gemm_up",
+        "config": {"workload": f"grouped MoE experts: {E} experts, {Mt} routed rows (8192 tokens x top-8, "
+                               f"Dirichlet(0.5)), up {Ku}->{Nu}, down {Kd}->{Nd}", "E": E, "rows": Mt},
+    }
+    return step, info
+
+
+def setup_decode(torch, fb, dev):
+    """Decode-shaped grouped GEMM: 32 experts, 1..256 rows each, weights pre-quantized."""
+    import workloads
+    d = workloads.decode_grouped(device=dev)
+    off = torch.from_numpy(d["offsets"]).to(dev)
+    Mt = int(d["offsets"][-1])
+    E, N, K = d["W"].shape
+    qw, sw = _quantized_experts(torch, fb, dev, d.pop("W"))
+    qa, sa = fb.fp8_quant_act_1x128(d["A"])
+    # second weight copy so consecutive steps do not hit the Infinity Cache
+    qw2, sw2 = qw.clone(), sw.clone()
+    C = torch.empty((Mt, N), dtype=torch.bfloat16, device=dev)
+    L = fb.lib()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    state = {"i": 0}
+
+    def step(timer):
+        w, s = (qw, sw) if state["i"] % 2 == 0 else (qw2, sw2)
+        state["i"] += 1
+        timer.mark()
+        rc = L.fp8_grouped_gemm_blockscaled(qa.data_ptr(), sa.data_ptr(), w.data_ptr(), s.data_ptr(),
+                                            C.data_ptr(), off.data_ptr(), E, Mt, N, K, stream)
+        timer.mark()
+        if rc:
+            raise RuntimeError(f"libfp8bs call failed ({rc})")
+
+    nbytes = E * N * K + Mt * K + Mt * N * 2 + E * (N // 128) * (K // 128) * 4 + (K // 128) * Mt * 4
+    info = {
+        "names": ["grouped_gemm_decode"],
+        "step_flops": 2.0 * Mt * N * K,
+        "step_bytes": nbytes,
+        "work": {"grouped_gemm_decode": ("GB/s", nbytes)},
+        "dominant": "grouped_gemm_decode",
+        "config": {"workload": f"decode grouped GEMM: {E} experts, {Mt} rows (1..256 per expert), "
+                               f"K={K}, N={N}, weights pre-quantized", "E": E, "rows": Mt},
+    }
+    return step, info
+
+
+WORKLOADS = {"dense_fprop": setup_dense_fprop, "backward": setup_backward, "moe": setup_moe,
+             "decode": setup_decode}
+
+
+# ---------------------------------------------------------------------------
+# CPU oracle baseline (bounded sample of the same step)
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(workload):
+    import numpy as np
+    import torch
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max(i.get("num_threads", 1) for i in threadpool_info())
+    except Exception:
+        cores = os.cpu_count()
+    g = torch.Generator().manual_seed(0)
+    if workload == "decode":
+        # one expert of the decode GEMM: 256 rows x 4096 x 7168, weights pre-quantized
+        M, N, K = 256, 4096, 7168
+        A = torch.randn(M, K, generator=g).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        W = (torch.randn(N, K, generator=g) * 0.01).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        qw, sw = oracle.quant_w_128x128(W)
+        qa, sa = oracle.quant_act_1x128(A)
+        t0 = time.perf_counter()
+        oracle.gemm_ref(qa, sa, qw, sw)
+        dt = time.perf_counter() - t0
+        nbytes = N * K + M * K + M * N * 2
+        return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
+                "sample": f"one decode expert: GEMM {M}x{N}x{K} (pre-quantized operands), {dt:.1f} s"}
+    M, N, K = 1024, 4096, 7168
+    X = torch.randn(M, K, generator=g).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    W = (torch.randn(N, K, generator=g) * 0.006).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    t0 = time.perf_counter()
+    qx, sx = oracle.quant_act_1x128(X)
+    qw, sw = oracle.quant_w_128x128(W)
+    oracle.gemm_ref(qx, sx, qw, sw)
+    dt = time.perf_counter() - t0
+    return {"value": 2.0 * M * N * K / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"one Fprop step at {M}x{N}x{K}: quantize X 1x128 and W 128x128, GEMM; {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", choices=sorted(WORKLOADS), default="dense_fprop")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import fp8_block_scaled_x1_amd as fb
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    fb.lib()   # fails loudly if the HIP library is missing
+    dev = torch.device("cuda:0")
+    step, info = WORKLOADS[args.workload](torch, fb, dev)
+    names = info["names"]
+
+    warm = Timer(torch, names, 0)
+    for _ in range(args.warmup):
+        step(warm)
+    torch.cuda.synchronize()
+    timer = Timer(torch, names, args.steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(timer)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    per_kernel = timer.averages_us()
+    kernels = {}
+    for n in names:
+        unit, work = info["work"][n]
+        us = per_kernel[n]
+        rate = work / (us * 1e-6) / (1e12 if unit == "TFLOP/s" else 1e9)
+        peak = PEAK_FP8_TFLOPS if unit == "TFLOP/s" else PEAK_HBM_GBS
+        kernels[n] = {"us": round(us, 2), unit: round(rate, 1), "frac_of_peak": round(rate / peak, 4)}
+
+    dom = info["dominant"]
+    unit, work = info["work"][dom]
+    achieved = work / (per_kernel[dom] * 1e-6) / (1e12 if unit == "TFLOP/s" else 1e9)
+    peak = PEAK_FP8_TFLOPS if unit == "TFLOP/s" else PEAK_HBM_GBS
+    roofline = {"bound": "mfma" if unit == "TFLOP/s" else "hbm", "achieved": round(achieved, 1), "peak": peak,
+                "unit": unit, "frac": round(achieved / peak, 4),
+                "traffic": measured_traffic(dom, args.workload), "kernel": dom,
+                "work_per_launch": work}
+
+    if "step_bytes" in info:
+        value, vunit = info["step_bytes"] / (ms_per_step * 1e-3) / 1e9, "GB/s"
+    else:
+        value, vunit = info["step_flops"] / (ms_per_step * 1e-3) / 1e12, "TFLOP/s"
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": vunit, "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3 (fp32 accumulate, bf16 out)",
+        "data": "synthetic (seeded; shapes and distributions of the workload)",
+        "config": info["config"], "kernels": kernels, "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(args.workload)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
