@@ -305,7 +305,23 @@ def setup_decode(torch, fb, dev):
     return step, info
 
 
-WORKLOADS = {"dense_fprop": setup_dense_fprop, "backward": setup_backward, "moe": setup_moe,
+def setup_copy(torch, fb, dev, nbytes=1 << 30):
+    """A plain device-to-device copy of known size (calibrates HBM byte counters)."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+
+    def step(timer):
+        timer.mark()
+        dst.copy_(src)
+        timer.mark()
+
+    info = {"names": ["copy"], "step_flops": 0.0, "step_bytes": 2 * nbytes,
+            "work": {"copy": ("GB/s", 2 * nbytes)}, "dominant": "copy",
+            "config": {"workload": f"device copy of {nbytes} bytes (counter calibration)", "bytes": nbytes}}
+    return step, info
+
+
+WORKLOADS = {"copy": setup_copy, "dense_fprop": setup_dense_fprop, "backward": setup_backward, "moe": setup_moe,
              "decode": setup_decode}
 
 
@@ -324,6 +340,8 @@ def cpu_baseline(workload):
     except Exception:
         cores = os.cpu_count()
     g = torch.Generator().manual_seed(0)
+    if workload == "copy":
+        return None
     if workload == "decode":
         # one expert of the decode GEMM: 256 rows x 4096 x 7168, weights pre-quantized
         M, N, K = 256, 4096, 7168
@@ -415,7 +433,7 @@ def main():
         "data": "synthetic (seeded; shapes and distributions of the workload)",
         "config": info["config"], "kernels": kernels, "roofline": roofline,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.workload != "copy":
         line["cpu_baseline"] = cpu_baseline(args.workload)
     print(json.dumps(line), flush=True)
 
