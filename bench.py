@@ -305,8 +305,9 @@ def setup_decode(torch, fb, dev):
     return step, info
 
 
-def setup_copy(torch, fb, dev, nbytes=1 << 30):
+def setup_copy(torch, fb, dev, nbytes=None):
     """A plain device-to-device copy of known size (calibrates HBM byte counters)."""
+    nbytes = nbytes or int(os.environ.get("BENCH_COPY_BYTES", 1 << 30))
     src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
     dst = torch.empty_like(src)
 

@@ -45,7 +45,7 @@ int fp8_quant_act_1x128(const void* x, int dtype, int64_t M, int64_t K, uint8_t*
                         void* stream) {
   if (!valid_dtype(dtype)) return FP8BS_ERR_DTYPE;
   if (M < 0 || K < 0 || K % kG) return FP8BS_ERR_SHAPE;
-  if (K >= kI32 || (M > 0 && K > 0 && ((M + 3) / 4) * (K / kG) >= kI32)) return FP8BS_ERR_TOO_LARGE;
+  if (K >= kI32 || (M + 15) / 16 > 65535 || K / kG >= kI32) return FP8BS_ERR_TOO_LARGE;
   if (M == 0 || K == 0) return FP8BS_OK;
   if (!x || !q || !s) return FP8BS_ERR_NULL_PTR;
   if (misaligned(x) || misaligned(q) || misaligned(s)) return FP8BS_ERR_ALIGN;

@@ -38,6 +38,56 @@ __device__ __forceinline__ uint32_t e4m3_code(float y) {
   return mag | sign;
 }
 
+// Four values -> four E4M3 codes packed little-endian in one dword, with the
+// hardware converter (v_cvt_pk_fp8_f32, OCP E4M3 on gfx950, round to nearest
+// even). An exhaustive run over every finite FP32 bit pattern on MI355X gave
+// results identical to e4m3_code() above for all |y| < 464, the converter
+// returning NaN above that; the clamp to +-448 first (which keeps -0 as -0)
+// turns that range into the saturated code 0x7E / 0xFE that e4m3_code gives.
+__device__ __forceinline__ uint32_t e4m3_pack4(float y0, float y1, float y2, float y3) {
+  y0 = __builtin_amdgcn_fmed3f(y0, -kE4M3Max, kE4M3Max);
+  y1 = __builtin_amdgcn_fmed3f(y1, -kE4M3Max, kE4M3Max);
+  y2 = __builtin_amdgcn_fmed3f(y2, -kE4M3Max, kE4M3Max);
+  y3 = __builtin_amdgcn_fmed3f(y3, -kE4M3Max, kE4M3Max);
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y2, y3, lo, true);
+}
+
+// Codes of x[i] / s for four values, identical to e4m3_pack4(x[i] / s) with
+// IEEE division, at a fraction of the cost. r must be RN(1/s) and s_fast must
+// say whether s lies in [2^-126, 2^125] (s and r normal).
+//
+// Why it is exact: q0 = RN(x * r) carries two roundings of at most 2^-24
+// relative each, so |q0 - x/s| < 2.0001 ulp of x/s, which is at most 5 steps
+// of the FP32 grid around q0 even where the spacing halves at a power of two;
+// RN(x/s) is therefore one of the FP32 values within 6 steps of q0. The E4M3
+// encoding is monotonic, so if the values 6 steps below and above q0 encode to
+// the same code, every candidate does, RN(x/s) included, and that code is the
+// code of q0. Otherwise (q0 near an E4M3 rounding boundary, rare) the lane
+// recomputes with the IEEE division. A zero q0 has the sign of x and encodes
+// to the signed zero code, which is also what any value that small gives.
+// With s normal, |x/s| <= 448*(1 + 2^-23), so q0 + 6 ulp stays far below 464,
+// where the converter stops saturating.
+__device__ __forceinline__ uint32_t e4m3_div_pack4(float x0, float x1, float x2, float x3, float s, float r,
+                                                   bool s_fast) {
+  const float q0 = x0 * r, q1 = x1 * r, q2 = x2 * r, q3 = x3 * r;
+  const float q[4] = {q0, q1, q2, q3};
+  bool ok = s_fast;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t b = __float_as_uint(q[i]);
+    const uint32_t nb = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(__uint_as_float(b - 6u), __uint_as_float(b + 6u), 0, false);
+    ok = ok && (((nb ^ (nb >> 8)) & 0xFFu) == 0u || q[i] == 0.0f);
+  }
+  if (__builtin_expect(ok, 1)) {
+    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(q0, q1, 0, false);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q2, q3, lo, true);
+  }
+  return e4m3_pack4(x0 / s, x1 / s, x2 / s, x3 / s);
+}
+
+__device__ __forceinline__ bool scale_is_fast(float s) { return s >= 0x1p-126f && s <= 0x1p125f; }
+
 __device__ __forceinline__ float bf16_bits_to_float(uint32_t b16) {
   return __uint_as_float(b16 << 16);
 }

@@ -42,61 +42,55 @@ __device__ __forceinline__ void load8(const void* base, int64_t elem, float v[8]
   }
 }
 
-__device__ __forceinline__ uint2 cast8(const float v[8], float s) {
-  uint32_t c[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) c[i] = e4m3_code(v[i] / s);
-  return make_uint2(pack4(c[0], c[1], c[2], c[3]), pack4(c[4], c[5], c[6], c[7]));
+// codes of v[i] / s (IEEE FP32 division, then E4M3); r = RN(1/s)
+__device__ __forceinline__ uint2 cast8(const float v[8], float s, float r, bool fast) {
+  return make_uint2(e4m3_div_pack4(v[0], v[1], v[2], v[3], s, r, fast),
+                    e4m3_div_pack4(v[4], v[5], v[6], v[7], s, r, fast));
 }
 
 // ---------------------------------------------------------------------------
 // 1x128 activation quantizer.
-// A wave handles 4 groups at once: rows 4*mq .. 4*mq+3 of one K chunk kb.
-// Lane l: row 4*mq + l/16, elements kb*128 + (l%16)*8 .. +7. The 16 lanes of a
-// DPP row form one group, so amax is a 4-step row rotation. Each wave does
-// kUnroll consecutive chunks of the same rows to keep loads in flight.
+// Block of 4 waves: rows 16*by .. 16*by+15 (wave w: rows 16*by + 4w + l/16),
+// K chunks kActSteps*bx .. +kActSteps-1 (chunk blocks of the same rows are
+// dispatched back to back, so DRAM pages are read in long runs). Lane l covers
+// elements (l%16)*8 .. +7 of its row's chunk, so the 16 lanes of a DPP row form
+// one group and amax is a 4-step row rotation. All of a lane's loads are
+// issued before any compute (row and chunk indices are clamped, stores masked),
+// so every lane keeps kActSteps 16-byte (BF16) or 32-byte (F32) loads in flight.
 // ---------------------------------------------------------------------------
-constexpr int kActUnroll = 2;
+constexpr int kActSteps = 4;
 
 template <bool BF16>
 __global__ __launch_bounds__(256) void quant_act_1x128_kernel(
     const void* __restrict__ x, int64_t M, int K, uint8_t* __restrict__ q,
-    float* __restrict__ s, uint32_t wave_tasks) {
+    float* __restrict__ s) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const uint32_t nkb = (uint32_t)K / kGroup;
+  const int nkb = K / kGroup;
   const int part = lane & 15;
-  const uint32_t wt0 = (blockIdx.x * 4u + wave) * kActUnroll;
+  const int64_t row = ((int64_t)blockIdx.y * 4 + wave) * 4 + (lane >> 4);
+  const int64_t rowc = row < M ? row : M - 1;
+  const int kb0 = blockIdx.x * kActSteps;
+  const int64_t base = rowc * K + part * 8;
 
-  float v[kActUnroll][8];
-  int64_t row[kActUnroll];
-  uint32_t kb[kActUnroll];
-  bool live[kActUnroll];
+  float v[kActSteps][8];
 #pragma unroll
-  for (int u = 0; u < kActUnroll; ++u) {
-    const uint32_t wt = wt0 + u;
-    const uint32_t mq = wt / nkb;
-    kb[u] = wt - mq * nkb;
-    row[u] = (int64_t)mq * 4 + (lane >> 4);
-    live[u] = wt < wave_tasks && row[u] < M;
-    if (live[u]) {
-      load8<BF16>(x, row[u] * K + kb[u] * kGroup + part * 8, v[u]);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v[u][i] = 0.0f;
-    }
+  for (int u = 0; u < kActSteps; ++u) {
+    const int kb = min(kb0 + u, nkb - 1);
+    load8<BF16>(x, base + kb * kGroup, v[u]);
   }
 #pragma unroll
-  for (int u = 0; u < kActUnroll; ++u) {
+  for (int u = 0; u < kActSteps; ++u) {
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[u][i]));
     amax = row16_max(amax);
     const float sc = group_scale(amax);
-    const uint2 codes = cast8(v[u], sc);
-    if (live[u]) {
-      *reinterpret_cast<uint2*>(q + row[u] * K + kb[u] * kGroup + part * 8) = codes;
-      if (part == 0) s[(int64_t)kb[u] * M + row[u]] = sc;
+    const uint2 codes = cast8(v[u], sc, 1.0f / sc, scale_is_fast(sc));
+    const int kb = kb0 + u;
+    if (row < M && kb < nkb) {
+      *reinterpret_cast<uint2*>(q + row * K + kb * kGroup + part * 8) = codes;
+      if (part == 0) s[(int64_t)kb * M + row] = sc;
     }
   }
 }
@@ -137,11 +131,13 @@ __global__ __launch_bounds__(256) void quant_w_128x128_kernel(
   __syncthreads();
   amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   const float sc = group_scale(amax);
+  const float rc = 1.0f / sc;
+  const bool fast = scale_is_fast(sc);
 
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int rl = i * 16 + r0;
-    const uint2 codes = cast8(v[i], sc);
+    const uint2 codes = cast8(v[i], sc, rc, fast);
     *reinterpret_cast<uint2*>(q + ((int64_t)nb * kGroup + rl) * K + (int64_t)kb * kGroup + part * 8) = codes;
     if constexpr (TRANS) {
       uint32_t* d = reinterpret_cast<uint32_t*>(tile + rl * kTileStride + part * 8);
@@ -248,13 +244,13 @@ __global__ __launch_bounds__(256) void quant_act_128x1_T_kernel(
   }
   __syncthreads();
   const float s0 = scl[2 * cp], s1 = scl[2 * cp + 1];
+  const float r0 = 1.0f / s0, r1 = 1.0f / s1;
+  const bool f0 = scale_is_fast(s0), f1 = scale_is_fast(s1);
   uint32_t w0[4], w1[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    w0[j] = pack4(e4m3_code(v0[4 * j] / s0), e4m3_code(v0[4 * j + 1] / s0),
-                  e4m3_code(v0[4 * j + 2] / s0), e4m3_code(v0[4 * j + 3] / s0));
-    w1[j] = pack4(e4m3_code(v1[4 * j] / s1), e4m3_code(v1[4 * j + 1] / s1),
-                  e4m3_code(v1[4 * j + 2] / s1), e4m3_code(v1[4 * j + 3] / s1));
+    w0[j] = e4m3_div_pack4(v0[4 * j], v0[4 * j + 1], v0[4 * j + 2], v0[4 * j + 3], s0, r0, f0);
+    w1[j] = e4m3_div_pack4(v1[4 * j], v1[4 * j + 1], v1[4 * j + 2], v1[4 * j + 3], s1, r1, f1);
   }
   if (ok0) *reinterpret_cast<uint4*>(qT + (int64_t)ch * M + tok0) = make_uint4(w0[0], w0[1], w0[2], w0[3]);
   if (ok1) *reinterpret_cast<uint4*>(qT + (int64_t)(ch + 1) * M + tok0) = make_uint4(w1[0], w1[1], w1[2], w1[3]);
@@ -265,16 +261,12 @@ __global__ __launch_bounds__(256) void quant_act_128x1_T_kernel(
 // ---------------------------------------------------------------------------
 hipError_t launch_quant_act_1x128(const void* x, bool bf16, int64_t M, int64_t K, uint8_t* q,
                                   float* s, hipStream_t stream) {
-  const uint32_t nkb = (uint32_t)(K / kGroup);
-  const uint32_t wave_tasks = (uint32_t)((M + 3) / 4) * nkb;
-  const uint32_t per_block = 4 * kActUnroll;
-  const uint32_t blocks = (wave_tasks + per_block - 1) / per_block;
+  const int64_t nkb = K / kGroup;
+  const dim3 grid((unsigned)((nkb + kActSteps - 1) / kActSteps), (unsigned)((M + 15) / 16));
   if (bf16)
-    hipLaunchKernelGGL(quant_act_1x128_kernel<true>, dim3(blocks), dim3(256), 0, stream, x, M,
-                       (int)K, q, s, wave_tasks);
+    hipLaunchKernelGGL(quant_act_1x128_kernel<true>, grid, dim3(256), 0, stream, x, M, (int)K, q, s);
   else
-    hipLaunchKernelGGL(quant_act_1x128_kernel<false>, dim3(blocks), dim3(256), 0, stream, x, M,
-                       (int)K, q, s, wave_tasks);
+    hipLaunchKernelGGL(quant_act_1x128_kernel<false>, grid, dim3(256), 0, stream, x, M, (int)K, q, s);
   return hipGetLastError();
 }
 
