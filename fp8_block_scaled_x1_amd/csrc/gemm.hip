@@ -55,26 +55,33 @@ constexpr int kThreads = 512;        // 8 waves
 constexpr int kGroupM = 8;           // tile-order grouping for L2 reuse
 constexpr int kXcds = 8;
 
-template <int BM_, int BN_, int WGM_, int WGN_>
+template <int BM_, int BN_, int WGM_, int WGN_, int DA_, int DB_>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_;
+  static constexpr int DA = DA_, DB = DB_;                    // ring depth per operand
   static constexpr int WM = BM / WGM, WN = BN / WGN;          // wave subtile
   static constexpr int MS = WM / 16, NS = WN / 16;            // MFMA tiles per wave
-  static constexpr int kABytes = BM * BK, kBBytes = BN * BK;
-  static constexpr int kScaleOfs = kABytes + kBBytes;         // then sA[BM], sB[BN] floats
-  static constexpr int kStageBytes = kScaleOfs + (BM + BN) * 4;
-  static constexpr int kSlices = (BM + BN) / 8;               // 1 KB load slices per stage
-  static constexpr int kSlicesPerWave = (kSlices + 7) / 8;
+  // one ring slot: the operand's 128-wide K chunk, then its scale vector
+  // (sA[BM]; sB[BN] in row mode) padded to whole 64-float pieces
+  static constexpr int kAPieces = (BM + 63) / 64, kBPieces = (BN + 63) / 64;  // scale loads
+  static constexpr int kASlot = BM * BK + 256 * kAPieces, kBSlot = BN * BK + 256 * kBPieces;
+  static constexpr int kBRing = DA * kASlot;                  // B ring follows the A ring
+  static constexpr int kLdsBytes = DA * kASlot + DB * kBSlot;
+  static constexpr int kASlices = BM / 8, kBSlices = BN / 8;  // 1 KB load slices per chunk
+  static constexpr int kASlicesPerWave = (kASlices + 7) / 8, kBSlicesPerWave = (kBSlices + 7) / 8;
   static constexpr bool kHoldB = NS <= MS;                    // hold the smaller operand
   static_assert(WGM * WGN == 8, "8 waves");
   static_assert(WM % 16 == 0 && WN % 16 == 0 && BM % 8 == 0 && BN % 8 == 0, "tile shape");
-  static_assert(2 * kStageBytes <= 160 * 1024, "LDS");
+  static_assert(DA >= 2 && DB >= 2 && DA + DB <= 5, "at most one operand three deep");
+  static_assert(kAPieces <= 4 && kBPieces <= 4, "scale loads");
+  static_assert(kLdsBytes <= 160 * 1024, "LDS");
 };
 
-// 256x256, waves 2x4 of 128x64; 256x224, waves 4x2 of 64x112; 224x256, waves 2x4 of 112x64
-using Cfg256x256 = Cfg<256, 256, 2, 4>;
-using Cfg256x224 = Cfg<256, 224, 4, 2>;
-using Cfg224x256 = Cfg<224, 256, 2, 4>;
+// 256x256, waves 2x4 of 128x64, both operands two deep;
+// 256x224, waves 4x2 of 64x112, A three deep; 224x256, waves 2x4 of 112x64, B three deep
+using Cfg256x256 = Cfg<256, 256, 2, 4, 2, 2>;
+using Cfg256x224 = Cfg<256, 224, 4, 2, 3, 2>;
+using Cfg224x256 = Cfg<224, 256, 2, 4, 2, 3>;
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
@@ -161,60 +168,87 @@ struct Tile {
   int n0, N, K;
 };
 
+// Wait until at most N of this wave's vector-memory operations are pending
+// (direct-to-LDS loads complete in issue order) and all its LDS reads and
+// scalar loads have returned, then meet the other waves at the barrier. The
+// memory clobber keeps the compiler from moving LDS accesses across it.
+template <int N>
+__device__ __forceinline__ void wait_and_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
 template <class G, int ROW_MODE>
-__device__ __forceinline__ void run_tile(const Tile& t, uint8_t* stage0, uint8_t* stage1) {
+__device__ __forceinline__ void run_tile(const Tile& t, uint8_t* smem) {
   constexpr int MS = G::MS, NS = G::NS, WM = G::WM, WN = G::WN;
-  constexpr int SLA = G::BM / 8;                         // A slices come first
+  constexpr bool kDeepA = G::DA == 3, kDeepB = G::DB == 3, kDeep = kDeepA || kDeepB;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  __builtin_assume(wave >= 0 && wave < 8);
   const int wm = wave / G::WGN, wn = wave % G::WGN;
   const int nkb = t.K / BK;
   const int a_last = t.row_end - 1;
   const int b_last = t.N - 1;
 
-  // Direct-to-LDS operand loads. Slice s (1 KB) covers tile rows 8s .. 8s+7 of
-  // A (s < BM/8) or of B; this wave loads slices wave, wave+8, ... Lane p
-  // fetches row 8s + p/8, logical 16-byte column (p%8) ^ swz(row), and writes
-  // physical column p%8. Offsets are 32-bit from a uniform base (M*K,
-  // N*K < 2^31); rows past the end are clamped (their results are never stored).
-  uint32_t offs[G::kSlicesPerWave];
-#pragma unroll
-  for (int j = 0; j < G::kSlicesPerWave; ++j) {
-    const int s = wave + 8 * j;
-    const bool isA = s < SLA;
-    const int rr = (isA ? s : s - SLA) * 8 + (lane >> 3);
+  // Direct-to-LDS operand loads. Slice s (1 KB) of an operand covers its tile
+  // rows 8s .. 8s+7; this wave loads slices wave, wave+8, ... Lane p fetches
+  // row 8s + p/8, logical 16-byte column (p%8) ^ swz(row), and writes physical
+  // column p%8. Offsets are 32-bit from a uniform base (M*K, N*K < 2^31); rows
+  // past the end are clamped (their results are never stored). A wave whose
+  // last slice index is past the tile repeats its previous slice (same bytes
+  // to the same place), so every wave issues the same number of loads.
+  auto slice_of = [&](int j, int slices) { return wave + 8 * j < slices ? wave + 8 * j : wave + 8 * (j - 1); };
+  auto slice_off = [&](int s, int first, int last) {
+    const int rr = s * 8 + (lane >> 3);
     const uint32_t col = (uint32_t)(((lane & 7) ^ swz(rr)) << 4);
-    const int row = isA ? min(t.m0 + rr, a_last) : min(t.n0 + rr, b_last);
-    offs[j] = (uint32_t)row * (uint32_t)t.K + col;
+    return (uint32_t)min(first + rr, last) * (uint32_t)t.K + col;
+  };
+  constexpr int kAL = G::kASlicesPerWave, kBL = G::kBSlicesPerWave;
+  uint32_t aoffs[kAL], boffs[kBL], alds[kAL], blds[kBL];
+#pragma unroll
+  for (int j = 0; j < kAL; ++j) {
+    const int sl = slice_of(j, G::kASlices);
+    aoffs[j] = slice_off(sl, t.m0, a_last);
+    alds[j] = (uint32_t)sl * 1024u;
   }
-  // Scale vectors: sA[kb][m0 .. m0+BM-1] by wave 0 and, in row mode,
-  // sB[kb][n0 .. n0+BN-1] by wave 1, 64 floats per 4-byte load, clamped.
-  uint32_t soff[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
-    soff[j] = 4u * (uint32_t)(wave == 0 ? min(t.m0 + 64 * j + lane, a_last) : min(t.n0 + 64 * j + lane, b_last));
+  for (int j = 0; j < kBL; ++j) {
+    const int sl = slice_of(j, G::kBSlices);
+    boffs[j] = slice_off(sl, t.n0, b_last);
+    blds[j] = (uint32_t)sl * 1024u;
+  }
+  // Scale vectors: piece q = (7 - wave) mod pieces (64 floats, one 4-byte load
+  // per lane) of sA[kb][m0 ..] and, in row mode, of sB[kb][n0 ..]; rows are
+  // clamped, lanes past the tile write into the slot's padding, and pieces
+  // loaded by two waves carry the same bytes.
+  const int qa = (7 - wave) % G::kAPieces, qb = (7 - wave) % G::kBPieces;
+  const uint32_t sa_off = 4u * (uint32_t)min(t.m0 + 64 * qa + lane, a_last);
+  const uint32_t sb_off = 4u * (uint32_t)min(t.n0 + 64 * qb + lane, b_last);
+  // loads per wave per chunk of each operand
+  constexpr int kNA = kAL + 1, kNB = kBL + (ROW_MODE ? 1 : 0);
 
-  auto issue_stage = [&](int kb, uint32_t st) {
-    const uint8_t* Ak = t.A + (int64_t)kb * BK;
-    const uint8_t* Bk = t.B + (int64_t)kb * BK;
+  const uint32_t lds = lds_addr_of(smem);
+  // j-th load of this wave for operand A (B) of chunk kb into ring slot `slot`
+  auto a_load = [&](int j, int kb, int slot) {
+    const uint32_t st = lds + (uint32_t)(slot * G::kASlot);
+    if (j < kAL)
+      lds_dma16(t.A + (int64_t)kb * BK, aoffs[j], st + alds[j]);
+    else
+      lds_dma4(t.sA + (int64_t)kb * t.sa_stride, sa_off, st + (uint32_t)(G::BM * BK + 256 * qa));
+  };
+  auto b_load = [&](int j, int kb, int slot) {
+    const uint32_t st = lds + (uint32_t)(G::kBRing + slot * G::kBSlot);
+    if (j < kBL)
+      lds_dma16(t.B + (int64_t)kb * BK, boffs[j], st + blds[j]);
+    else
+      lds_dma4(t.sB + (int64_t)kb * t.N, sb_off, st + (uint32_t)(G::BN * BK + 256 * qb));
+  };
+  auto issue_a = [&](int kb, int slot) {
 #pragma unroll
-    for (int j = 0; j < G::kSlicesPerWave; ++j) {
-      const int s = wave + 8 * j;
-      if (s < G::kSlices) lds_dma16(s < SLA ? Ak : Bk, offs[j], st + (uint32_t)s * 1024u);
-    }
-    if (wave == 0) {
-      const float* sk = t.sA + (int64_t)kb * t.sa_stride;
+    for (int j = 0; j < kNA; ++j) a_load(j, kb, slot);
+  };
+  auto issue_b = [&](int kb, int slot) {
 #pragma unroll
-      for (int j = 0; j < (G::BM + 63) / 64; ++j)
-        if (64 * j + lane < G::BM) lds_dma4(sk, soff[j], st + (uint32_t)G::kScaleOfs + j * 256u);
-    } else if (ROW_MODE && wave == 1) {
-      const float* sk = t.sB + (int64_t)kb * t.N;
-#pragma unroll
-      for (int j = 0; j < (G::BN + 63) / 64; ++j)
-        if (64 * j + lane < G::BN)
-          lds_dma4(sk, soff[j], st + (uint32_t)(G::kScaleOfs + G::BM * 4) + j * 256u);
-    }
+    for (int j = 0; j < kNB; ++j) b_load(j, kb, slot);
   };
 
   v4f acc[MS][NS];
@@ -229,115 +263,188 @@ __device__ __forceinline__ void run_tile(const Tile& t, uint8_t* stage0, uint8_t
   for (int j = 0; j < NS; ++j)
     sbb_ptr[j] = t.sB + (int64_t)(min(t.n0 + wn * WN + 16 * j, b_last) / BK) * nkb;
 
-  // One chunk: wait for its stage, start the next stage's loads into the other
-  // buffer, then compute.
-  auto chunk = [&](int kb, const uint8_t* st, uint32_t other) {
-    __builtin_amdgcn_s_waitcnt(0);      // this wave's direct-to-LDS loads landed
-    __syncthreads();                    // everyone's landed; everyone finished the other stage
-    if (kb + 1 < nkb) issue_stage(kb + 1, other);
-    const uint8_t* As = st;
-    const uint8_t* Bs = st + G::kABytes;
-    const float* sAs = reinterpret_cast<const float*>(st + G::kScaleOfs) + wm * WM + (lane & 15);
-    const float* sBs = reinterpret_cast<const float*>(st + G::kScaleOfs + G::BM * 4) + wn * WN + 4 * (lane >> 4);
+  // The fragments of the smaller operand ("held", NH of them) are read once per
+  // chunk; those of the other ("streamed", NT) one step ahead of their use.
+  // Step t issues the MFMAs of streamed subtile t against every held subtile,
+  // then the promotion of step t-1, so each promotion waits on MFMAs issued a
+  // whole step earlier.
+  constexpr bool HA = !G::kHoldB;                 // A held, B streamed
+  constexpr int NH = HA ? MS : NS, NT = HA ? NS : MS;
+  const int h_sub = HA ? wm * MS : wn * NS;       // first held / streamed subtile
+  const int t_sub = HA ? wn * NS : wm * MS;
 
+  // Per-lane scale values. sa: the lane's A row of subtile i (sA of the chunk,
+  // staged in LDS); sb: block mode one uniform value per n-subtile, row mode the
+  // lane's four columns of n-subtile j.
+  struct Scales {
+    float sa[MS];
     float sbb[NS];
     float sbr[NS][4];
+  };
+
+  auto slot_a = [&](int kb) { return smem + (kb % G::DA) * G::kASlot; };
+  auto slot_b = [&](int kb) { return smem + G::kBRing + (kb % G::DB) * G::kBSlot; };
+  auto read_t = [&](int kb, int t) {
+    return read_frag(HA ? slot_b(kb) : slot_a(kb), t_sub + t, lane);
+  };
+  auto read_chunk_start = [&](int kb, v8i (&hf)[NH], v8i& tf, Scales& sc) {
+    const uint8_t* As = slot_a(kb);
+    const uint8_t* Bs = slot_b(kb);
+#pragma unroll
+    for (int h = 0; h < NH; ++h) hf[h] = read_frag(HA ? As : Bs, h_sub + h, lane);
+    tf = read_t(kb, 0);
+    const float* sAs = reinterpret_cast<const float*>(As + G::BM * BK) + wm * WM + (lane & 15);
+    const float* sBs = reinterpret_cast<const float*>(Bs + G::BN * BK) + wn * WN + 4 * (lane >> 4);
+#pragma unroll
+    for (int i = 0; i < MS; ++i) sc.sa[i] = sAs[16 * i];
     if constexpr (ROW_MODE) {
 #pragma unroll
       for (int j = 0; j < NS; ++j) {
         const float4 v = *reinterpret_cast<const float4*>(sBs + 16 * j);
-        sbr[j][0] = v.x; sbr[j][1] = v.y; sbr[j][2] = v.z; sbr[j][3] = v.w;
+        sc.sbr[j][0] = v.x; sc.sbr[j][1] = v.y; sc.sbr[j][2] = v.z; sc.sbr[j][3] = v.w;
       }
     } else {
 #pragma unroll
-      for (int j = 0; j < NS; ++j) sbb[j] = sbb_ptr[j][kb];
-    }
-
-    // promotion of MFMA tile (i, j): scaled FP32 partial into the FP32 accumulator
-    auto promote = [&](int i, int j, const v4f& p, float sa) {
-      if constexpr (ROW_MODE) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[i][j][r] = fmaf(p[r] * sbr[j][r], sa, acc[i][j][r]);
-      } else {
-        const float sc = sa * sbb[j];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[i][j][r] = fmaf(p[r], sc, acc[i][j][r]);
-      }
-    };
-
-    if constexpr (G::kHoldB) {
-      // hold the NS B fragments, stream the MS A subtiles
-      v8i bf[NS];
-#pragma unroll
-      for (int j = 0; j < NS; ++j) bf[j] = read_frag(Bs, wn * NS + j, lane);
-      v4f p_prev[NS];
-      float sa_prev = 0.f;
-      v8i af = read_frag(As, wm * MS, lane);
-#pragma unroll
-      for (int i = 0; i <= MS; ++i) {
-        v4f p_cur[NS];
-        float sa_cur = 0.f;
-        if (i < MS) {
-          const v8i a_now = af;
-          if (i + 1 < MS) af = read_frag(As, wm * MS + i + 1, lane);
-          sa_cur = sAs[16 * i];
-#pragma unroll
-          for (int j = 0; j < NS; ++j)
-            p_cur[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], a_now, v4f{0.f, 0.f, 0.f, 0.f},
-                                                                        0, 0, 0, 0, 0, 0);
-        }
-        if (i > 0) {
-#pragma unroll
-          for (int j = 0; j < NS; ++j) promote(i - 1, j, p_prev[j], sa_prev);
-        }
-        if (i < MS) {
-#pragma unroll
-          for (int j = 0; j < NS; ++j) p_prev[j] = p_cur[j];
-          sa_prev = sa_cur;
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    } else {
-      // hold the MS A fragments (and their scales), stream the NS B subtiles
-      v8i af[MS];
-      float sa[MS];
-#pragma unroll
-      for (int i = 0; i < MS; ++i) {
-        af[i] = read_frag(As, wm * MS + i, lane);
-        sa[i] = sAs[16 * i];
-      }
-      v4f p_prev[MS];
-      v8i bf = read_frag(Bs, wn * NS, lane);
-#pragma unroll
-      for (int j = 0; j <= NS; ++j) {
-        v4f p_cur[MS];
-        if (j < NS) {
-          const v8i b_now = bf;
-          if (j + 1 < NS) bf = read_frag(Bs, wn * NS + j + 1, lane);
-#pragma unroll
-          for (int i = 0; i < MS; ++i)
-            p_cur[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b_now, af[i], v4f{0.f, 0.f, 0.f, 0.f},
-                                                                        0, 0, 0, 0, 0, 0);
-        }
-        if (j > 0) {
-#pragma unroll
-          for (int i = 0; i < MS; ++i) promote(i, j - 1, p_prev[i], sa[i]);
-        }
-        if (j < NS) {
-#pragma unroll
-          for (int i = 0; i < MS; ++i) p_prev[i] = p_cur[i];
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
+      for (int j = 0; j < NS; ++j) sc.sbb[j] = sbb_ptr[j][kb];
     }
   };
+  // promotion of MFMA tile (i, j): scaled FP32 partial into the FP32 accumulator
+  auto promote = [&](int i, int j, const v4f& p, const Scales& sc) {
+    if constexpr (ROW_MODE) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[i][j][r] = fmaf(p[r] * sc.sbr[j][r], sc.sa[i], acc[i][j][r]);
+    } else {
+      const float f = sc.sa[i] * sc.sbb[j];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[i][j][r] = fmaf(p[r], f, acc[i][j][r]);
+    }
+  };
+  auto promote_step = [&](int t, const v4f (&p)[NH], const Scales& sc) {
+#pragma unroll
+    for (int h = 0; h < NH; ++h) promote(HA ? h : t, HA ? t : h, p[h], sc);
+  };
 
-  const uint32_t lds0 = lds_addr_of(stage0), lds1 = lds_addr_of(stage1);
-  issue_stage(0, lds0);
-  for (int kb = 0; kb < nkb; kb += 2) {
-    chunk(kb, stage0, lds1);
-    if (kb + 1 < nkb) chunk(kb + 1, stage1, lds0);
+  // Chunk x is readable after barrier x. Before it each wave waits for its own
+  // loads of chunk x and for its LDS reads of chunk x-1, so after it every
+  // wave's loads of chunk x are visible and chunk x-1's slots are free. While
+  // chunk x is computed they are refilled, a few loads per step so that no
+  // wave stalls on a full load queue: first the shallow operand's chunk x+1,
+  // then the deep operand's chunk x+2 (both operands' chunk x+1 without a
+  // deep ring, in the first half of the steps). Only the deep operand's loads,
+  // issued last, may still be in flight at the next barrier. Chunk indices
+  // past the end are clamped: those loads land in free slots and go unused.
+  constexpr int kND = kDeepA ? kNA : kDeepB ? kNB : 0;   // deep loads per chunk
+  constexpr int kItems = kNA + kNB;
+  constexpr int kSpread = kDeep ? NT : (NT + 1) / 2;
+  auto barrier = [&](int x) {
+    if (kDeep && x < nkb)
+      wait_and_barrier<kND>();
+    else
+      wait_and_barrier<0>();
+  };
+  // load k (0 <= k < kItems) of the refill issued while chunk kb is computed
+  auto refill_load = [&](int k, int kb) {
+    const int k1 = min(kb + 1, nkb - 1), k2 = min(kb + 2, nkb - 1);
+    if constexpr (kDeepA) {
+      if (k < kNB) b_load(k, k1, (kb + 1) % G::DB);
+      else a_load(k - kNB, k2, (kb + 2) % G::DA);
+    } else if constexpr (kDeepB) {
+      if (k < kNA) a_load(k, k1, (kb + 1) % G::DA);
+      else b_load(k - kNA, k2, (kb + 2) % G::DB);
+    } else {
+      if (k < kNA) a_load(k, k1, (kb + 1) % G::DA);
+      else b_load(k - kNA, k1, (kb + 1) % G::DB);
+    }
+  };
+  auto refill_step = [&](int t, int kb) {
+#pragma unroll
+    for (int k = 0; k < kItems; ++k)
+      if (k * kSpread / kItems == t) refill_load(k, kb);
+  };
+
+  // prologue: chunk 0 of both operands, chunk 1 of a three-deep operand
+  issue_a(0, 0);
+  issue_b(0, 0);
+  if constexpr (kDeepA) issue_a(min(1, nkb - 1), 1);
+  if constexpr (kDeepB) issue_b(min(1, nkb - 1), 1);
+  barrier(0);
+
+  v8i hf[NH];
+  v8i tf;
+  Scales sc;
+  read_chunk_start(0, hf, tf, sc);
+#ifndef CARRY
+#define CARRY 1
+#endif
+  // Block mode carries the promotion of a chunk's last step into the first
+  // step of the next chunk (zero partials before the first chunk), so every
+  // step interleaves MFMAs with promotions; row mode, short of registers for
+  // a second set of column scales, finishes it right after the barrier.
+  constexpr bool kCarry = CARRY && !ROW_MODE;
+  v4f p_prev[NH];
+  Scales sc_prev;
+  if constexpr (kCarry) {
+#pragma unroll
+    for (int h = 0; h < NH; ++h) p_prev[h] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < MS; ++i) sc_prev.sa[i] = 0.f;
+#pragma unroll
+    for (int j = 0; j < NS; ++j) sc_prev.sbb[j] = 0.f;
   }
+  for (int kb = 0; kb < nkb; ++kb) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      refill_step(t, kb);
+      v4f p_cur[NH];
+      const v8i t_now = tf;
+#pragma unroll
+      for (int h = 0; h < NH; ++h)
+        p_cur[h] = HA ? __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(t_now, hf[h], v4f{0.f, 0.f, 0.f, 0.f},
+                                                                         0, 0, 0, 0, 0, 0)
+                      : __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(hf[h], t_now, v4f{0.f, 0.f, 0.f, 0.f},
+                                                                         0, 0, 0, 0, 0, 0);
+      if (t + 1 < NT) tf = read_t(kb, t + 1);
+      const bool promoting = t > 0 || kCarry;
+      if (t > 0)
+        promote_step(t - 1, p_prev, sc);
+      else if (kCarry)
+        promote_step(NT - 1, p_prev, sc_prev);
+      // one MFMA, then a group of promotion FMAs, so the two pipes overlap
+      if (promoting) {
+#pragma unroll
+        for (int h = 0; h < NH; ++h) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (h == 0 && t + 1 < NT) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, ROW_MODE ? 8 : 6, 0);
+        }
+      }
+#pragma unroll
+      for (int h = 0; h < NH; ++h) p_prev[h] = p_cur[h];
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // Every LDS read of chunk kb is issued and the last step's MFMAs are in
+    // flight: cross the next chunk's barrier now and read its first fragments
+    // while they run. (After the last chunk the reads repeat it and go unused,
+    // which keeps the loop branch-free.) The promoted accumulators are pinned
+    // first so that the compiler cannot sink the promotions past the barrier.
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int h = 0; h < NH; ++h)
+        if (t + 1 < NT || kCarry) asm volatile("" : "+v"(acc[HA ? h : t][HA ? t : h]));
+    Scales sc_next;
+    barrier(kb + 1);
+    read_chunk_start(min(kb + 1, nkb - 1), hf, tf, sc_next);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (kCarry) {
+      sc_prev = sc;
+    } else {
+      promote_step(NT - 1, p_prev, sc);
+    }
+    sc = sc_next;
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if constexpr (kCarry) promote_step(NT - 1, p_prev, sc_prev);
 
   // BF16 epilogue, round to nearest even: lane holds C[m][n..n+3]
   const int m_lane = t.m0 + wm * WM + (lane & 15);
@@ -365,8 +472,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const uint8_t* __rest
                                                             const float* __restrict__ sB,
                                                             uint16_t* __restrict__ C, int M, int N,
                                                             int K) {
-  __shared__ __align__(16) uint8_t stage0[G::kStageBytes];
-  __shared__ __align__(16) uint8_t stage1[G::kStageBytes];
+  __shared__ __align__(16) uint8_t smem[G::kLdsBytes];
   const int tiles_m = (M + G::BM - 1) / G::BM, tiles_n = (N + G::BN - 1) / G::BN;
   const int pid = xcd_remap(blockIdx.x, gridDim.x);
   int tm, tn;
@@ -376,7 +482,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const uint8_t* __rest
   t.B = B; t.sB = sB; t.C = C;
   t.m0 = tm * G::BM; t.row_end = M;
   t.n0 = tn * G::BN; t.N = N; t.K = K;
-  run_tile<G, ROW_MODE>(t, stage0, stage1);
+  run_tile<G, ROW_MODE>(t, smem);
 }
 
 // Per-expert tiles: expert e owns rows [off[e], off[e+1]); its tiles are
@@ -387,8 +493,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ sA, const uint8_t* __restrict__ B,
     const float* __restrict__ sB, uint16_t* __restrict__ C, const int32_t* __restrict__ offsets,
     int E, int M_total, int N, int K) {
-  __shared__ __align__(16) uint8_t stage0[G::kStageBytes];
-  __shared__ __align__(16) uint8_t stage1[G::kStageBytes];
+  __shared__ __align__(16) uint8_t smem[G::kLdsBytes];
   const int tiles_n = (N + G::BN - 1) / G::BN;
   const int pid = xcd_remap(blockIdx.x, gridDim.x);
   int base = 0, e_found = -1, r0 = 0, r1 = 0;
@@ -413,7 +518,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
   t.C = C;
   t.m0 = r0 + tm * G::BM; t.row_end = r1;
   t.n0 = tn * G::BN; t.N = N; t.K = K;
-  run_tile<G, 0>(t, stage0, stage1);
+  run_tile<G, 0>(t, smem);
 }
 
 // Estimated cost of a tile shape: full rounds of tiles over the CUs times the
