@@ -40,6 +40,8 @@
 //   * the tile shape is chosen on the host per problem so that the number of
 //     tiles fills whole rounds of the 256 CUs where possible.
 
+#include <type_traits>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -257,11 +259,17 @@ __device__ __forceinline__ void run_tile(const Tile& t, uint8_t* smem) {
 #pragma unroll
     for (int j = 0; j < NS; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  // block mode: B scale of n-subtile j is sB[(n of the subtile)/128][kb], uniform
-  const float* sbb_ptr[NS];
-#pragma unroll
-  for (int j = 0; j < NS; ++j)
-    sbb_ptr[j] = t.sB + (int64_t)(min(t.n0 + wn * WN + 16 * j, b_last) / BK) * nkb;
+  // Block mode: the B scale of n-subtile j is sB[(n of the subtile)/128][kb],
+  // uniform over the subtile. A wave's WN <= 128 columns span at most two
+  // 128-column blocks: subtiles below `split` lie in the first, the rest in
+  // the second.
+  static_assert(WN <= BK, "a wave's columns span at most two scale blocks");
+  const int ncol0 = t.n0 + wn * WN;
+  const int blk_lo = min(ncol0, b_last) / BK;
+  const int blk_hi = min(blk_lo + 1, b_last / BK);
+  const int split = min(NS, (BK - (ncol0 & (BK - 1))) / 16);
+  const float* sbb_lo = t.sB + (int64_t)blk_lo * nkb;
+  const float* sbb_hi = t.sB + (int64_t)blk_hi * nkb;
 
   // The fragments of the smaller operand ("held", NH of them) are read once per
   // chunk; those of the other ("streamed", NT) one step ahead of their use.
@@ -276,10 +284,26 @@ __device__ __forceinline__ void run_tile(const Tile& t, uint8_t* smem) {
   // Per-lane scale values. sa: the lane's A row of subtile i (sA of the chunk,
   // staged in LDS); sb: block mode one uniform value per n-subtile, row mode the
   // lane's four columns of n-subtile j.
+  // Per-lane scale values of a chunk: sa[i] for the lane's A row of subtile i;
+  // row mode sbr[j] for its four columns of n-subtile j, block mode the B
+  // scales lo / hi of the wave's first and second 128-column block.
   struct Scales {
     float sa[MS];
-    float sbb[NS];
     float sbr[NS][4];
+    float lo, hi;
+  };
+  // Block mode: the products sa[i] * lo and sa[i] * hi, formed once per chunk.
+  struct Factors {
+    float flo[MS], fhi[MS];
+  };
+  auto factors = [&](const Scales& sc) {
+    Factors f;
+#pragma unroll
+    for (int i = 0; i < MS; ++i) {
+      f.flo[i] = sc.sa[i] * sc.lo;
+      f.fhi[i] = sc.sa[i] * sc.hi;
+    }
+    return f;
   };
 
   auto slot_a = [&](int kb) { return smem + (kb % G::DA) * G::kASlot; };
@@ -304,24 +328,25 @@ __device__ __forceinline__ void run_tile(const Tile& t, uint8_t* smem) {
         sc.sbr[j][0] = v.x; sc.sbr[j][1] = v.y; sc.sbr[j][2] = v.z; sc.sbr[j][3] = v.w;
       }
     } else {
-#pragma unroll
-      for (int j = 0; j < NS; ++j) sc.sbb[j] = sbb_ptr[j][kb];
+      sc.lo = sbb_lo[kb];
+      sc.hi = sbb_hi[kb];
     }
   };
-  // promotion of MFMA tile (i, j): scaled FP32 partial into the FP32 accumulator
-  auto promote = [&](int i, int j, const v4f& p, const Scales& sc) {
+  // promotion of MFMA tile (i, j): scaled FP32 partial into the FP32
+  // accumulator; S is the wave's block split (a compile-time constant)
+  auto promote = [&](int i, int j, const v4f& p, const Scales& sc, const Factors& fc, int S) {
     if constexpr (ROW_MODE) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc[i][j][r] = fmaf(p[r] * sc.sbr[j][r], sc.sa[i], acc[i][j][r]);
     } else {
-      const float f = sc.sa[i] * sc.sbb[j];
+      const float f = j < S ? fc.flo[i] : fc.fhi[i];
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc[i][j][r] = fmaf(p[r], f, acc[i][j][r]);
     }
   };
-  auto promote_step = [&](int t, const v4f (&p)[NH], const Scales& sc) {
+  auto promote_step = [&](int t, const v4f (&p)[NH], const Scales& sc, const Factors& fc, int S) {
 #pragma unroll
-    for (int h = 0; h < NH; ++h) promote(HA ? h : t, HA ? t : h, p[h], sc);
+    for (int h = 0; h < NH; ++h) promote(HA ? h : t, HA ? t : h, p[h], sc, fc, S);
   };
 
   // Chunk x is readable after barrier x. Before it each wave waits for its own
@@ -369,82 +394,108 @@ __device__ __forceinline__ void run_tile(const Tile& t, uint8_t* smem) {
   if constexpr (kDeepB) issue_b(min(1, nkb - 1), 1);
   barrier(0);
 
-  v8i hf[NH];
-  v8i tf;
-  Scales sc;
-  read_chunk_start(0, hf, tf, sc);
+  // The main loop, compiled once per block split that can occur.
+  auto main_loop = [&](auto split_c) {
+    constexpr int S = decltype(split_c)::value;
+    v8i hf[NH];
+    v8i tf;
+    Scales sc;
+    read_chunk_start(0, hf, tf, sc);
 #ifndef CARRY
 #define CARRY 1
 #endif
-  // Block mode carries the promotion of a chunk's last step into the first
-  // step of the next chunk (zero partials before the first chunk), so every
-  // step interleaves MFMAs with promotions; row mode, short of registers for
-  // a second set of column scales, finishes it right after the barrier.
-  constexpr bool kCarry = CARRY && !ROW_MODE;
-  v4f p_prev[NH];
-  Scales sc_prev;
-  if constexpr (kCarry) {
+    // Block mode carries the promotion of a chunk's last step into the first
+    // step of the next chunk (zero partials before the first chunk), so every
+    // step interleaves MFMAs with promotions; row mode, short of registers for
+    // a second set of column scales, finishes it right after the barrier.
+    constexpr bool kCarry = CARRY && !ROW_MODE;
+    v4f p_prev[NH];
+    Factors f_prev;
+    if constexpr (kCarry) {
 #pragma unroll
-    for (int h = 0; h < NH; ++h) p_prev[h] = v4f{0.f, 0.f, 0.f, 0.f};
+      for (int h = 0; h < NH; ++h) p_prev[h] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < MS; ++i) sc_prev.sa[i] = 0.f;
+      for (int i = 0; i < MS; ++i) f_prev.flo[i] = f_prev.fhi[i] = 0.f;
+    }
+    for (int kb = 0; kb < nkb; ++kb) {
+      Factors fc;
+      if constexpr (!ROW_MODE) fc = factors(sc);
 #pragma unroll
-    for (int j = 0; j < NS; ++j) sc_prev.sbb[j] = 0.f;
-  }
-  for (int kb = 0; kb < nkb; ++kb) {
+      for (int t = 0; t < NT; ++t) {
+        refill_step(t, kb);
+        v4f p_cur[NH];
+        const v8i t_now = tf;
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      refill_step(t, kb);
-      v4f p_cur[NH];
-      const v8i t_now = tf;
+        for (int h = 0; h < NH; ++h)
+          p_cur[h] = HA ? __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(t_now, hf[h], v4f{0.f, 0.f, 0.f, 0.f},
+                                                                           0, 0, 0, 0, 0, 0)
+                        : __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(hf[h], t_now, v4f{0.f, 0.f, 0.f, 0.f},
+                                                                           0, 0, 0, 0, 0, 0);
+        if (t + 1 < NT) tf = read_t(kb, t + 1);
+        const bool promoting = t > 0 || kCarry;
+        if (t > 0)
+          promote_step(t - 1, p_prev, sc, fc, S);
+        else if (kCarry)
+          promote_step(NT - 1, p_prev, sc, f_prev, S);
+        // one MFMA, then a group of promotion FMAs, so the two pipes overlap
+        if (promoting) {
 #pragma unroll
-      for (int h = 0; h < NH; ++h)
-        p_cur[h] = HA ? __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(t_now, hf[h], v4f{0.f, 0.f, 0.f, 0.f},
-                                                                         0, 0, 0, 0, 0, 0)
-                      : __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(hf[h], t_now, v4f{0.f, 0.f, 0.f, 0.f},
-                                                                         0, 0, 0, 0, 0, 0);
-      if (t + 1 < NT) tf = read_t(kb, t + 1);
-      const bool promoting = t > 0 || kCarry;
-      if (t > 0)
-        promote_step(t - 1, p_prev, sc);
-      else if (kCarry)
-        promote_step(NT - 1, p_prev, sc_prev);
-      // one MFMA, then a group of promotion FMAs, so the two pipes overlap
-      if (promoting) {
-#pragma unroll
-        for (int h = 0; h < NH; ++h) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          if (h == 0 && t + 1 < NT) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, ROW_MODE ? 8 : 6, 0);
+          for (int h = 0; h < NH; ++h) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (h == 0 && t + 1 < NT) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, ROW_MODE ? 8 : 6, 0);
+          }
         }
-      }
 #pragma unroll
-      for (int h = 0; h < NH; ++h) p_prev[h] = p_cur[h];
+        for (int h = 0; h < NH; ++h) p_prev[h] = p_cur[h];
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // Every LDS read of chunk kb is issued and the last step's MFMAs are in
+      // flight: cross the next chunk's barrier now and read its first fragments
+      // while they run. (After the last chunk the reads repeat it and go unused,
+      // which keeps the loop branch-free.) The promoted accumulators are pinned
+      // first so that the compiler cannot sink the promotions past the barrier.
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int h = 0; h < NH; ++h)
+          if (t + 1 < NT || kCarry) asm volatile("" : "+v"(acc[HA ? h : t][HA ? t : h]));
+      Scales sc_next;
+      barrier(kb + 1);
+      read_chunk_start(min(kb + 1, nkb - 1), hf, tf, sc_next);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (kCarry) {
+        f_prev = fc;
+      } else {
+        promote_step(NT - 1, p_prev, sc, fc, S);
+      }
+      sc = sc_next;
       __builtin_amdgcn_sched_barrier(0);
     }
-    // Every LDS read of chunk kb is issued and the last step's MFMAs are in
-    // flight: cross the next chunk's barrier now and read its first fragments
-    // while they run. (After the last chunk the reads repeat it and go unused,
-    // which keeps the loop branch-free.) The promoted accumulators are pinned
-    // first so that the compiler cannot sink the promotions past the barrier.
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-      for (int h = 0; h < NH; ++h)
-        if (t + 1 < NT || kCarry) asm volatile("" : "+v"(acc[HA ? h : t][HA ? t : h]));
-    Scales sc_next;
-    barrier(kb + 1);
-    read_chunk_start(min(kb + 1, nkb - 1), hf, tf, sc_next);
-    __builtin_amdgcn_sched_barrier(0);
-    if constexpr (kCarry) {
-      sc_prev = sc;
-    } else {
-      promote_step(NT - 1, p_prev, sc);
+    if constexpr (kCarry) promote_step(NT - 1, p_prev, sc, f_prev, S);
+  };
+  if constexpr (ROW_MODE || (G::BN % BK == 0 && BK % WN == 0)) {
+    main_loop(std::integral_constant<int, NS>{});   // every wave within one block
+  } else {
+    switch (split) {
+#define FP8BS_SPLIT_CASE(v) \
+  case v:                   \
+    if constexpr (v < NS) { \
+      main_loop(std::integral_constant<int, v>{}); \
+      break;                \
     }
-    sc = sc_next;
-    __builtin_amdgcn_sched_barrier(0);
+      FP8BS_SPLIT_CASE(1)
+      FP8BS_SPLIT_CASE(2)
+      FP8BS_SPLIT_CASE(3)
+      FP8BS_SPLIT_CASE(4)
+      FP8BS_SPLIT_CASE(5)
+      FP8BS_SPLIT_CASE(6)
+      FP8BS_SPLIT_CASE(7)
+#undef FP8BS_SPLIT_CASE
+      default:
+        main_loop(std::integral_constant<int, NS>{});
+    }
   }
-  if constexpr (kCarry) promote_step(NT - 1, p_prev, sc_prev);
 
   // BF16 epilogue, round to nearest even: lane holds C[m][n..n+3]
   const int m_lane = t.m0 + wm * WM + (lane & 15);
