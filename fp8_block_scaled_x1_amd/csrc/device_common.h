@@ -60,33 +60,41 @@ __device__ __forceinline__ uint32_t e4m3_pack4(float y0, float y1, float y2, flo
 // Why it is exact: q0 = RN(x * r) carries two roundings of at most 2^-24
 // relative each, so |q0 - x/s| < 2.0001 ulp of x/s, which is at most 5 steps
 // of the FP32 grid around q0 even where the spacing halves at a power of two;
-// RN(x/s) is therefore one of the FP32 values within 6 steps of q0. The E4M3
-// encoding is monotonic, so if the values 6 steps below and above q0 encode to
-// the same code, every candidate does, RN(x/s) included, and that code is the
-// code of q0. Otherwise (q0 near an E4M3 rounding boundary, rare) the lane
-// recomputes with the IEEE division. A zero q0 has the sign of x and encodes
-// to the signed zero code, which is also what any value that small gives.
-// With s normal, |x/s| <= 448*(1 + 2^-23), so q0 + 6 ulp stays far below 464,
-// where the converter stops saturating.
+// |RN(x/s)| is therefore one of the FP32 magnitudes within 6 steps of |q0|
+// (down to zero), and RN(x/s) has the sign of q0 (the sign of x, s > 0). The
+// E4M3 encoding of a magnitude is monotonic and the code of a signed value is
+// its sign bit over the code of its magnitude, so if the magnitudes 6 steps
+// below (saturating at zero) and 6 steps above |q0| encode to the same code,
+// every candidate does and the code of q0 is the code of RN(x/s). Otherwise
+// (q0 near an E4M3 rounding boundary, rare) the lane recomputes with the IEEE
+// division. With s normal, |x/s| <= 448*(1 + 2^-23), so |q0| + 6 steps stays
+// far below 464, where the converter stops saturating. The check is straight
+// line code: two neighbour codes per value from one conversion, compared four
+// bytes at a time.
 __device__ __forceinline__ uint32_t e4m3_div_pack4(float x0, float x1, float x2, float x3, float s, float r,
                                                    bool s_fast) {
   const float q0 = x0 * r, q1 = x1 * r, q2 = x2 * r, q3 = x3 * r;
   const float q[4] = {q0, q1, q2, q3};
-  bool ok = s_fast;
+  float lo[4], hi[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const uint32_t b = __float_as_uint(q[i]);
-    const uint32_t nb = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(__uint_as_float(b - 6u), __uint_as_float(b + 6u), 0, false);
-    ok = ok && (((nb ^ (nb >> 8)) & 0xFFu) == 0u || q[i] == 0.0f);
+    const uint32_t m = __float_as_uint(q[i]) & 0x7FFFFFFFu;
+    lo[i] = __uint_as_float(__builtin_elementwise_sub_sat(m, 6u));
+    hi[i] = __uint_as_float(m + 6u);
   }
-  if (__builtin_expect(ok, 1)) {
-    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(q0, q1, 0, false);
-    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q2, q3, lo, true);
+  // bytes: code(lo0) code(hi0) code(lo1) code(hi1), and the same for 2, 3
+  const uint32_t n01 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(
+      lo[1], hi[1], __builtin_amdgcn_cvt_pk_fp8_f32(lo[0], hi[0], 0, false), true);
+  const uint32_t n23 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(
+      lo[3], hi[3], __builtin_amdgcn_cvt_pk_fp8_f32(lo[2], hi[2], 0, false), true);
+  const uint32_t bad = ((n01 ^ (n01 >> 8)) | (n23 ^ (n23 >> 8))) & 0x00FF00FFu;
+  if (__builtin_expect(s_fast & (bad == 0u), 1)) {
+    const int c01 = __builtin_amdgcn_cvt_pk_fp8_f32(q0, q1, 0, false);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q2, q3, c01, true);
   }
   return e4m3_pack4(x0 / s, x1 / s, x2 / s, x3 / s);
 }
 
-__device__ __forceinline__ bool scale_is_fast(float s) { return s >= 0x1p-126f && s <= 0x1p125f; }
 
 __device__ __forceinline__ float bf16_bits_to_float(uint32_t b16) {
   return __uint_as_float(b16 << 16);
@@ -98,10 +106,83 @@ __device__ __forceinline__ uint32_t float_to_bf16_bits(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-// Group scale from the group's amax: amax / 448 (IEEE division), 1.0 if zero.
+// Group scale from the group's amax: amax / 448 rounded to nearest (the IEEE
+// quotient), 1.0 if zero. Where the quotient is a normal number it is formed
+// as q0 = RN(amax * RN(1/448)) plus one FMA correction; a sweep over every
+// positive finite FP32 amax on MI355X gave the IEEE quotient bit for bit
+// wherever that quotient is normal. Below that the IEEE division runs.
 __device__ __forceinline__ float group_scale(float amax) {
-  const float s = amax / kE4M3Max;
+  constexpr float c = 1.0f / kE4M3Max;
+  float s;
+  if (__builtin_expect(amax >= 0x1.cp-118f, 1)) {   // 448 * 2^-126
+    const float q0 = amax * c;
+    s = fmaf(fmaf(-q0, kE4M3Max, amax), c, q0);
+  } else {
+    s = amax / kE4M3Max;
+  }
   return s == 0.0f ? 1.0f : s;
+}
+
+// RN(1/s) for s in [2^-126, 2^125]: the hardware reciprocal estimate and one
+// Newton step; a sweep over every FP32 s in that range on MI355X gave the IEEE
+// quotient 1/s bit for bit. Outside that range the result is not used.
+__device__ __forceinline__ float recip_rn(float s) {
+  const float y0 = __builtin_amdgcn_rcpf(s);
+  return fmaf(fmaf(-s, y0, 1.0f), y0, y0);
+}
+
+// Per-group division state: the scale, RN(1/scale) and whether the fast
+// quotient paths below apply to it.
+struct GroupDiv {
+  float s, r;
+  bool fast;
+};
+// BF16 inputs use the one-correction quotient, which is exact for scales in
+// [2^-64, 2^125]; F32 inputs use the checked quotient, exact for [2^-126, 2^125].
+template <bool BF16>
+__device__ __forceinline__ GroupDiv group_div_of_scale(float s) {
+  GroupDiv g;
+  g.s = s;
+  g.r = recip_rn(s);
+  g.fast = s >= (BF16 ? 0x1p-64f : 0x1p-126f) && s <= 0x1p125f;
+  return g;
+}
+template <bool BF16>
+__device__ __forceinline__ GroupDiv group_div(float amax) {
+  return group_div_of_scale<BF16>(group_scale(amax));
+}
+
+// Codes of x[i] / s for four values taken from BF16 inputs, identical to
+// e4m3_pack4(x[i] / s) with IEEE division when s lies in [2^-64, 2^125] and
+// r = RN(1/s). The quotient is q0 = RN(x * r) with one FMA correction,
+// fma(x - q0 * s, r, q0), where the residual x - q0 * s is one FMA too, given
+// the sign of x (the correction turns -0 into +0). The result is
+// not always the correctly rounded FP32 quotient, but a sweep over every pair
+// of a positive finite BF16 amax and a BF16 x with |x| <= amax on MI355X, with
+// s = RN(amax / 448) in that range, gave the E4M3 code of the IEEE quotient in
+// every case. Outside the range the IEEE division runs.
+__device__ __forceinline__ uint32_t e4m3_div_pack4_bf16(float x0, float x1, float x2, float x3, const GroupDiv& g) {
+  if (__builtin_expect(g.fast, 1)) {
+    const float x[4] = {x0, x1, x2, x3};
+    float q[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float q0 = x[i] * g.r;
+      q[i] = __builtin_copysignf(fmaf(fmaf(-q0, g.s, x[i]), g.r, q0), x[i]);
+    }
+    const int c01 = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], c01, true);
+  }
+  return e4m3_pack4(x0 / g.s, x1 / g.s, x2 / g.s, x3 / g.s);
+}
+
+// The quotient codes for the input type: checked for F32, one-correction for BF16.
+template <bool BF16>
+__device__ __forceinline__ uint32_t e4m3_div_pack4_t(float x0, float x1, float x2, float x3, const GroupDiv& g) {
+  if constexpr (BF16)
+    return e4m3_div_pack4_bf16(x0, x1, x2, x3, g);
+  else
+    return e4m3_div_pack4(x0, x1, x2, x3, g.s, g.r, g.fast);
 }
 
 // Max over the 16 lanes of a DPP row (lanes 16r..16r+15), result in every lane

@@ -42,10 +42,11 @@ __device__ __forceinline__ void load8(const void* base, int64_t elem, float v[8]
   }
 }
 
-// codes of v[i] / s (IEEE FP32 division, then E4M3); r = RN(1/s)
-__device__ __forceinline__ uint2 cast8(const float v[8], float s, float r, bool fast) {
-  return make_uint2(e4m3_div_pack4(v[0], v[1], v[2], v[3], s, r, fast),
-                    e4m3_div_pack4(v[4], v[5], v[6], v[7], s, r, fast));
+// codes of v[i] / s (IEEE FP32 division, then E4M3)
+template <bool BF16>
+__device__ __forceinline__ uint2 cast8(const float v[8], const GroupDiv& g) {
+  return make_uint2(e4m3_div_pack4_t<BF16>(v[0], v[1], v[2], v[3], g),
+                    e4m3_div_pack4_t<BF16>(v[4], v[5], v[6], v[7], g));
 }
 
 // ---------------------------------------------------------------------------
@@ -85,8 +86,9 @@ __global__ __launch_bounds__(256) void quant_act_1x128_kernel(
 #pragma unroll
     for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[u][i]));
     amax = row16_max(amax);
-    const float sc = group_scale(amax);
-    const uint2 codes = cast8(v[u], sc, 1.0f / sc, scale_is_fast(sc));
+    const GroupDiv g = group_div<BF16>(amax);
+    const float sc = g.s;
+    const uint2 codes = cast8<BF16>(v[u], g);
     const int kb = kb0 + u;
     if (row < M && kb < nkb) {
       *reinterpret_cast<uint2*>(q + row * K + kb * kGroup + part * 8) = codes;
@@ -130,14 +132,13 @@ __global__ __launch_bounds__(256) void quant_w_128x128_kernel(
   if ((t & 63) == 0) red[t >> 6] = amax;
   __syncthreads();
   amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  const float sc = group_scale(amax);
-  const float rc = 1.0f / sc;
-  const bool fast = scale_is_fast(sc);
+  const GroupDiv g = group_div<BF16>(amax);
+  const float sc = g.s;
 
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int rl = i * 16 + r0;
-    const uint2 codes = cast8(v[i], sc, rc, fast);
+    const uint2 codes = cast8<BF16>(v[i], g);
     *reinterpret_cast<uint2*>(q + ((int64_t)nb * kGroup + rl) * K + (int64_t)kb * kGroup + part * 8) = codes;
     if constexpr (TRANS) {
       uint32_t* d = reinterpret_cast<uint32_t*>(tile + rl * kTileStride + part * 8);
@@ -243,14 +244,12 @@ __global__ __launch_bounds__(256) void quant_act_128x1_T_kernel(
     if (c0 + t < C) sT[(int64_t)tb * C + c0 + t] = sc;
   }
   __syncthreads();
-  const float s0 = scl[2 * cp], s1 = scl[2 * cp + 1];
-  const float r0 = 1.0f / s0, r1 = 1.0f / s1;
-  const bool f0 = scale_is_fast(s0), f1 = scale_is_fast(s1);
+  const GroupDiv g0 = group_div_of_scale<BF16>(scl[2 * cp]), g1 = group_div_of_scale<BF16>(scl[2 * cp + 1]);
   uint32_t w0[4], w1[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    w0[j] = e4m3_div_pack4(v0[4 * j], v0[4 * j + 1], v0[4 * j + 2], v0[4 * j + 3], s0, r0, f0);
-    w1[j] = e4m3_div_pack4(v1[4 * j], v1[4 * j + 1], v1[4 * j + 2], v1[4 * j + 3], s1, r1, f1);
+    w0[j] = e4m3_div_pack4_t<BF16>(v0[4 * j], v0[4 * j + 1], v0[4 * j + 2], v0[4 * j + 3], g0);
+    w1[j] = e4m3_div_pack4_t<BF16>(v1[4 * j], v1[4 * j + 1], v1[4 * j + 2], v1[4 * j + 3], g1);
   }
   if (ok0) *reinterpret_cast<uint4*>(qT + (int64_t)ch * M + tok0) = make_uint4(w0[0], w0[1], w0[2], w0[3]);
   if (ok1) *reinterpret_cast<uint4*>(qT + (int64_t)(ch + 1) * M + tok0) = make_uint4(w1[0], w1[1], w1[2], w1[3]);
