@@ -104,16 +104,17 @@ def _check_t(x_cpu, dev, what):
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
-@pytest.mark.parametrize("M,C", [(128, 1), (128, 64), (256, 63), (384, 130), (128, 7168)])
+@pytest.mark.parametrize("M,C", [(128, 1), (128, 64), (256, 63), (384, 130), (256, 72), (128, 200), (128, 7168)])
 def test_quant_act_128x1_T_shapes(dev, dtype, M, C):
     _check_t(_rand((M, C), M + 7 * C, dtype), dev, f"128x1 {dtype} {M}x{C}")
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
-def test_quant_act_128x1_T_adversarial(dev, dtype):
+@pytest.mark.parametrize("channels", [70, 72])   # the 16-byte-load kernel takes C % 8 == 0
+def test_quant_act_128x1_T_adversarial(dev, dtype, channels):
     # groups of the 128x1 quantizer run down columns: transpose adversarial rows
-    cols = np.ascontiguousarray(adversarial_rows(70, 384, seed=9).T)   # [384 tokens][70 channels]
-    _check_t(torch.from_numpy(cols).to(dtype), dev, f"128x1 adversarial {dtype}")
+    cols = np.ascontiguousarray(adversarial_rows(channels, 384, seed=9).T)   # [384 tokens][C channels]
+    _check_t(torch.from_numpy(cols).to(dtype), dev, f"128x1 adversarial {dtype} C={channels}")
 
 
 def test_quant_act_128x1_T_backward_workload(dev):
