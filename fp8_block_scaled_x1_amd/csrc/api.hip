@@ -45,7 +45,8 @@ int fp8_quant_act_1x128(const void* x, int dtype, int64_t M, int64_t K, uint8_t*
                         void* stream) {
   if (!valid_dtype(dtype)) return FP8BS_ERR_DTYPE;
   if (M < 0 || K < 0 || K % kG) return FP8BS_ERR_SHAPE;
-  if (K >= kI32 || (M + 15) / 16 > 65535 || K / kG >= kI32) return FP8BS_ERR_TOO_LARGE;
+  // grid: x over groups of 4 chunks, (y, z) over blocks of 8 rows
+  if (K >= kI32 || (M + 7) / 8 >= (int64_t)1 << 27 || (K / kG + 3) / 4 > 65535) return FP8BS_ERR_TOO_LARGE;
   if (M == 0 || K == 0) return FP8BS_OK;
   if (!x || !q || !s) return FP8BS_ERR_NULL_PTR;
   if (misaligned(x) || misaligned(q) || misaligned(s)) return FP8BS_ERR_ALIGN;

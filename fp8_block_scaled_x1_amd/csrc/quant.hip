@@ -51,15 +51,16 @@ __device__ __forceinline__ uint2 cast8(const float v[8], const GroupDiv& g) {
 
 // ---------------------------------------------------------------------------
 // 1x128 activation quantizer.
-// Block of 4 waves: rows 16*by .. 16*by+15 (wave w: rows 16*by + 4w + l/16),
-// K chunks kActSteps*bx .. +kActSteps-1 (chunk blocks of the same rows are
-// dispatched back to back, so DRAM pages are read in long runs). Lane l covers
-// elements (l%16)*8 .. +7 of its row's chunk, so the 16 lanes of a DPP row form
-// one group and amax is a 4-step row rotation. All of a lane's loads are
-// issued before any compute (row and chunk indices are clamped, stores masked),
-// so every lane keeps kActSteps 16-byte (BF16) or 32-byte (F32) loads in flight.
+// Block of 4 waves: rows 8*rb .. 8*rb+7 (wave w: rows 8*rb + 2w, 8*rb + 2w + 1)
+// with rb = blockIdx.y + gridDim.y * blockIdx.z, K chunks 4*bx .. 4*bx+3 (the
+// fastest grid index, so consecutive workgroups read consecutive 1 KB pieces
+// of the same rows). Lane l covers elements (l%16)*8 .. +7 of chunk
+// 4*bx + l/16, so each load instruction reads 1 KB of one row and the 16 lanes
+// of a DPP row form one group (amax is a 4-step row rotation). Both loads of a
+// lane are issued before any compute (row and chunk indices are clamped,
+// stores masked).
 // ---------------------------------------------------------------------------
-constexpr int kActSteps = 4;
+constexpr int kActRows = 2;   // rows per wave
 
 template <bool BF16>
 __global__ __launch_bounds__(256) void quant_act_1x128_kernel(
@@ -69,30 +70,30 @@ __global__ __launch_bounds__(256) void quant_act_1x128_kernel(
   const int wave = threadIdx.x >> 6;
   const int nkb = K / kGroup;
   const int part = lane & 15;
-  const int64_t row = ((int64_t)blockIdx.y * 4 + wave) * 4 + (lane >> 4);
-  const int64_t rowc = row < M ? row : M - 1;
-  const int kb0 = blockIdx.x * kActSteps;
-  const int64_t base = rowc * K + part * 8;
+  const int kb = blockIdx.x * 4 + (lane >> 4);
+  const int kbc = min(kb, nkb - 1);
+  const int64_t rb = (int64_t)blockIdx.z * gridDim.y + blockIdx.y;
+  const int64_t row0 = (rb * 4 + wave) * kActRows;
+  if (row0 - wave * kActRows >= M) return;   // whole block past the last row
 
-  float v[kActSteps][8];
+  float v[kActRows][8];
 #pragma unroll
-  for (int u = 0; u < kActSteps; ++u) {
-    const int kb = min(kb0 + u, nkb - 1);
-    load8<BF16>(x, base + kb * kGroup, v[u]);
+  for (int u = 0; u < kActRows; ++u) {
+    const int64_t row = min(row0 + u, M - 1);
+    load8<BF16>(x, row * K + (int64_t)kbc * kGroup + part * 8, v[u]);
   }
 #pragma unroll
-  for (int u = 0; u < kActSteps; ++u) {
+  for (int u = 0; u < kActRows; ++u) {
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[u][i]));
     amax = row16_max(amax);
     const GroupDiv g = group_div<BF16>(amax);
-    const float sc = g.s;
     const uint2 codes = cast8<BF16>(v[u], g);
-    const int kb = kb0 + u;
+    const int64_t row = row0 + u;
     if (row < M && kb < nkb) {
-      *reinterpret_cast<uint2*>(q + row * K + kb * kGroup + part * 8) = codes;
-      if (part == 0) s[(int64_t)kb * M + row] = sc;
+      *reinterpret_cast<uint2*>(q + row * K + (int64_t)kb * kGroup + part * 8) = codes;
+      if (part == 0) s[(int64_t)kb * M + row] = g.s;
     }
   }
 }
@@ -323,7 +324,9 @@ __global__ __launch_bounds__(256) void quant_act_128x1_T_v8_kernel(
 hipError_t launch_quant_act_1x128(const void* x, bool bf16, int64_t M, int64_t K, uint8_t* q,
                                   float* s, hipStream_t stream) {
   const int64_t nkb = K / kGroup;
-  const dim3 grid((unsigned)((nkb + kActSteps - 1) / kActSteps), (unsigned)((M + 15) / 16));
+  const int64_t nrb = (M + 4 * kActRows - 1) / (4 * kActRows);
+  const int64_t gy = nrb < 65535 ? nrb : 65535;
+  const dim3 grid((unsigned)((nkb + 3) / 4), (unsigned)gy, (unsigned)((nrb + gy - 1) / gy));
   if (bf16)
     hipLaunchKernelGGL(quant_act_1x128_kernel<true>, grid, dim3(256), 0, stream, x, M, (int)K, q, s);
   else

@@ -75,6 +75,7 @@ enum fp8bs_status {
  *   q  [M][K]      uint8 E4M3 codes
  *   s  [K/128][M]  float32, s[kb][m] = amax(group)/448, 1.0 for a zero group
  * K must be a multiple of 128; any M >= 0 (M == 0 or K == 0: no-op).
+ * FP8BS_ERR_TOO_LARGE if M >= 2^30 - 8, K >= 2^31 or K/128 > 262140.
  */
 FP8BS_API int fp8_quant_act_1x128(const void* x, int dtype, int64_t M, int64_t K,
                         uint8_t* q, float* s, void* stream);
