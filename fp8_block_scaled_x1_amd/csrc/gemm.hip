@@ -84,6 +84,9 @@ struct Cfg {
 using Cfg256x256 = Cfg<256, 256, 2, 4, 2, 2>;
 using Cfg256x224 = Cfg<256, 224, 4, 2, 3, 2>;
 using Cfg224x256 = Cfg<224, 256, 2, 4, 2, 3>;
+// 128x256, waves 2x4 of 64x64, B three deep: grouped GEMMs with few rows per
+// group (decode), where B is the operand streamed from HBM
+using Cfg128x256 = Cfg<128, 256, 2, 4, 2, 3>;
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
@@ -635,12 +638,18 @@ hipError_t launch_grouped_gemm_blockscaled(const uint8_t* A, const float* sA, co
                                            int E, int64_t M_total, int64_t N, int64_t K,
                                            hipStream_t stream) {
   using namespace gemm;
-  using G = Cfg256x256;
   // every expert adds at most one partial m-tile beyond M_total / BM
-  const int64_t tiles = ((M_total + G::BM - 1) / G::BM + E) * ((N + G::BN - 1) / G::BN);
-  hipLaunchKernelGGL((grouped_gemm_kernel<G>), dim3((unsigned)tiles), dim3(kThreads), 0, stream, A,
-                     sA, B, sB, C, offsets, E, (int)M_total, (int)N, (int)K);
-  return hipGetLastError();
+  auto launch = [&](auto cfg) {
+    using G = decltype(cfg);
+    const int64_t tiles = ((M_total + G::BM - 1) / G::BM + E) * ((N + G::BN - 1) / G::BN);
+    hipLaunchKernelGGL((grouped_gemm_kernel<G>), dim3((unsigned)tiles), dim3(kThreads), 0, stream, A,
+                       sA, B, sB, C, offsets, E, (int)M_total, (int)N, (int)K);
+    return hipGetLastError();
+  };
+  // few rows per expert on average: half-height tiles waste fewer MFMAs on
+  // padding rows while each expert's weights are still read about once
+  if (M_total < (int64_t)E * 256) return launch(Cfg128x256{});
+  return launch(Cfg256x256{});
 }
 
 }  // namespace fp8bs
