@@ -74,7 +74,7 @@ struct Cfg {
   static constexpr bool kHoldB = NS <= MS;                    // hold the smaller operand
   static_assert(WGM * WGN == 8, "8 waves");
   static_assert(WM % 16 == 0 && WN % 16 == 0 && BM % 8 == 0 && BN % 8 == 0, "tile shape");
-  static_assert(DA >= 2 && DB >= 2 && DA + DB <= 5, "at most one operand three deep");
+  static_assert(DA >= 2 && DA <= 3 && DB >= 2 && DB <= 3, "rings two or three deep");
   static_assert(kAPieces <= 4 && kBPieces <= 4, "scale loads");
   static_assert(kLdsBytes <= 160 * 1024, "LDS");
 };
@@ -84,9 +84,9 @@ struct Cfg {
 using Cfg256x256 = Cfg<256, 256, 2, 4, 2, 2>;
 using Cfg256x224 = Cfg<256, 224, 4, 2, 3, 2>;
 using Cfg224x256 = Cfg<224, 256, 2, 4, 2, 3>;
-// 128x256, waves 2x4 of 64x64, B three deep: grouped GEMMs with few rows per
-// group (decode), where B is the operand streamed from HBM
-using Cfg128x256 = Cfg<128, 256, 2, 4, 2, 3>;
+// 128x256, waves 2x4 of 64x64, both operands three deep: grouped GEMMs with
+// few rows per group (decode), where B is the operand streamed from HBM
+using Cfg128x256d = Cfg<128, 256, 2, 4, 3, 3>;
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
@@ -356,12 +356,13 @@ __device__ __forceinline__ void run_tile(const Tile& t, uint8_t* smem) {
   // loads of chunk x and for its LDS reads of chunk x-1, so after it every
   // wave's loads of chunk x are visible and chunk x-1's slots are free. While
   // chunk x is computed they are refilled, a few loads per step so that no
-  // wave stalls on a full load queue: first the shallow operand's chunk x+1,
-  // then the deep operand's chunk x+2 (both operands' chunk x+1 without a
-  // deep ring, in the first half of the steps). Only the deep operand's loads,
-  // issued last, may still be in flight at the next barrier. Chunk indices
-  // past the end are clamped: those loads land in free slots and go unused.
-  constexpr int kND = kDeepA ? kNA : kDeepB ? kNB : 0;   // deep loads per chunk
+  // wave stalls on a full load queue: first a shallow operand's chunk x+1,
+  // then a deep operand's chunk x+2 (both operands' chunk x+1 without a deep
+  // ring, in the first half of the steps; both operands' chunk x+2 when both
+  // are three deep). Only the deep loads, issued last, may still be in flight
+  // at the next barrier. Chunk indices past the end are clamped: those loads
+  // land in free slots and go unused.
+  constexpr int kND = (kDeepA ? kNA : 0) + (kDeepB ? kNB : 0);   // deep loads per chunk
   constexpr int kItems = kNA + kNB;
   constexpr int kSpread = kDeep ? NT : (NT + 1) / 2;
   auto barrier = [&](int x) {
@@ -373,7 +374,10 @@ __device__ __forceinline__ void run_tile(const Tile& t, uint8_t* smem) {
   // load k (0 <= k < kItems) of the refill issued while chunk kb is computed
   auto refill_load = [&](int k, int kb) {
     const int k1 = min(kb + 1, nkb - 1), k2 = min(kb + 2, nkb - 1);
-    if constexpr (kDeepA) {
+    if constexpr (kDeepA && kDeepB) {
+      if (k < kNA) a_load(k, k2, (kb + 2) % G::DA);
+      else b_load(k - kNA, k2, (kb + 2) % G::DB);
+    } else if constexpr (kDeepA) {
       if (k < kNB) b_load(k, k1, (kb + 1) % G::DB);
       else a_load(k - kNB, k2, (kb + 2) % G::DA);
     } else if constexpr (kDeepB) {
@@ -550,17 +554,41 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
   __shared__ __align__(16) uint8_t smem[G::kLdsBytes];
   const int tiles_n = (N + G::BN - 1) / G::BN;
   const int pid = xcd_remap(blockIdx.x, gridDim.x);
+  // Find the expert of tile pid: lane l of every wave takes expert e0 + l of
+  // a batch of 64, counts its tiles, and a prefix sum over the lanes finds
+  // the first expert whose tiles reach past pid (all offsets of a batch are
+  // loaded at once, not one dependent load per expert).
+  const int lane = threadIdx.x & 63;
   int base = 0, e_found = -1, r0 = 0, r1 = 0;
-  for (int e = 0; e < E; ++e) {
-    const int a = min(max(offsets[e], 0), M_total);
-    const int b = min(max(offsets[e + 1], a), M_total);
-    const int te = ((b - a + G::BM - 1) / G::BM) * tiles_n;
-    if (pid < base + te) {
-      e_found = e; r0 = a; r1 = b;
+  for (int e0 = 0; e0 < E; e0 += 64) {
+    const int e = e0 + lane;
+    int a = 0, b = 0, te = 0;
+    if (e < E) {
+      a = min(max(offsets[e], 0), M_total);
+      b = min(max(offsets[e + 1], a), M_total);
+      te = ((b - a + G::BM - 1) / G::BM) * tiles_n;
+    }
+    int incl = te;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int v = __shfl_up(incl, d, 64);
+      if (lane >= d) incl += v;
+    }
+    const uint64_t hit = __ballot(e < E && pid < base + incl);
+    if (hit) {
+      const int l = __ffsll((unsigned long long)hit) - 1;
+      e_found = e0 + l;
+      r0 = __shfl(a, l, 64);
+      r1 = __shfl(b, l, 64);
+      base += __shfl(incl, l, 64) - __shfl(te, l, 64);
       break;
     }
-    base += te;
+    base += __shfl(incl, 63, 64);
   }
+  e_found = __builtin_amdgcn_readfirstlane(e_found);
+  r0 = __builtin_amdgcn_readfirstlane(r0);
+  r1 = __builtin_amdgcn_readfirstlane(r1);
+  base = __builtin_amdgcn_readfirstlane(base);
   if (e_found < 0) return;
   int tm, tn;
   tile_coords(pid - base, (r1 - r0 + G::BM - 1) / G::BM, tiles_n, tm, tn);
@@ -646,9 +674,12 @@ hipError_t launch_grouped_gemm_blockscaled(const uint8_t* A, const float* sA, co
                        sA, B, sB, C, offsets, E, (int)M_total, (int)N, (int)K);
     return hipGetLastError();
   };
-  // few rows per expert on average: half-height tiles waste fewer MFMAs on
-  // padding rows while each expert's weights are still read about once
-  if (M_total < (int64_t)E * 256) return launch(Cfg128x256{});
+  // Few rows per expert on average (decode): half-height tiles waste fewer
+  // MFMAs on padding rows while each expert's weights are still read about
+  // once, and both operands three deep keep two chunks of weights in flight
+  // (the weights stream from HBM; a two-deep ring leaves every chunk waiting
+  // out a full HBM latency).
+  if (M_total < (int64_t)E * 256) return launch(Cfg128x256d{});
   return launch(Cfg256x256{});
 }
 
