@@ -6,8 +6,9 @@ default workload is the dense Fprop projection (X[4096][7168] BF16 quantized
 1x128, W[7168][7168] BF16 quantized 128x128, block-scaled FP8 GEMM with FP32
 promotion per 128-wide K chunk, BF16 output). Other workloads (--workload)
 measure the remaining forms of the path: the backward pair (Dgrad + Wgrad with
-the 128x1 transposed quantizer), the grouped MoE expert GEMMs and the
-decode-shaped grouped GEMM.
+the 128x1 transposed quantizer), the grouped MoE expert GEMMs, the
+decode-shaped grouped GEMM, and the Fprop whose GEMM writes the next layer's
+1x128-quantized input directly (fused quantizing epilogue).
 
 Prints one JSON line. `value` is whole-step throughput with inputs resident in
 HBM; `roofline` describes the dominant kernel, timed live with HIP events on
@@ -90,10 +91,13 @@ def _rotations(bytes_per_set, target=600e6):
     return max(2, int(-(-target // bytes_per_set)))
 
 
-def setup_dense_fprop(torch, fb, dev, M=4096, N=7168, K=7168):
+def setup_dense_fprop(torch, fb, dev, M=4096, N=7168, K=7168, fused=False):
+    """Quantize X 1x128 and W 128x128, then the GEMM. With fused=True the GEMM
+    writes the 1x128 quantization of its result (the next layer's FP8 input)
+    instead of the BF16 result."""
     import workloads
     sets = []
-    R = _rotations(M * K * 2 + N * K * 2 + M * K + N * K + M * N * 2)
+    R = _rotations(M * K * 2 + N * K * 2 + M * K + N * K + M * N * (1 if fused else 2))
     for r in range(R):
         d = workloads.dense_fprop(device=dev, seed=r, M=M, N=N, K=K)
         sets.append({
@@ -102,8 +106,12 @@ def setup_dense_fprop(torch, fb, dev, M=4096, N=7168, K=7168):
             "sx": torch.empty((K // 128, M), dtype=torch.float32, device=dev),
             "qw": torch.empty((N, K), dtype=torch.uint8, device=dev),
             "sw": torch.empty((N // 128, K // 128), dtype=torch.float32, device=dev),
-            "C": torch.empty((M, N), dtype=torch.bfloat16, device=dev),
         })
+        if fused:
+            sets[-1]["Q"] = torch.empty((M, N), dtype=torch.uint8, device=dev)
+            sets[-1]["sQ"] = torch.empty((N // 128, M), dtype=torch.float32, device=dev)
+        else:
+            sets[-1]["C"] = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     L = fb.lib()
     stream = torch.cuda.current_stream(dev).cuda_stream
     state = {"i": 0}
@@ -117,26 +125,38 @@ def setup_dense_fprop(torch, fb, dev, M=4096, N=7168, K=7168):
         rc |= L.fp8_quant_w_128x128(s["W"].data_ptr(), fb.BF16, N, K, s["qw"].data_ptr(), s["sw"].data_ptr(),
                                     None, None, stream)
         timer.mark()
-        rc |= L.fp8_gemm_blockscaled(s["qx"].data_ptr(), s["sx"].data_ptr(), s["qw"].data_ptr(),
-                                     s["sw"].data_ptr(), fb.SCALE_BLOCK128, s["C"].data_ptr(), M, N, K, stream)
+        if fused:
+            rc |= L.fp8_gemm_blockscaled_q1x128(s["qx"].data_ptr(), s["sx"].data_ptr(), s["qw"].data_ptr(),
+                                                s["sw"].data_ptr(), fb.SCALE_BLOCK128, s["Q"].data_ptr(),
+                                                s["sQ"].data_ptr(), M, N, K, stream)
+        else:
+            rc |= L.fp8_gemm_blockscaled(s["qx"].data_ptr(), s["sx"].data_ptr(), s["qw"].data_ptr(),
+                                         s["sw"].data_ptr(), fb.SCALE_BLOCK128, s["C"].data_ptr(), M, N, K, stream)
         timer.mark()
         if rc:
             raise RuntimeError(f"libfp8bs call failed ({rc})")
 
     flops = 2.0 * M * N * K
+    gemm = "gemm_blockscaled_q1x128" if fused else "gemm_blockscaled"
+    out = (f"Q[{M}x{N}] fp8 + sQ[{N // 128}x{M}] (fused 1x128 quantizing epilogue)" if fused
+           else f"C[{M}x{N}] bf16")
     info = {
-        "names": ["quant_act_1x128", "quant_w_128x128", "gemm_blockscaled"],
+        "names": ["quant_act_1x128", "quant_w_128x128", gemm],
         "step_flops": flops,
         "work": {
             "quant_act_1x128": ("GB/s", M * K * 2 + M * K + M * K // 128 * 4),
             "quant_w_128x128": ("GB/s", N * K * 2 + N * K + N * K // 16384 * 4),
-            "gemm_blockscaled": ("TFLOP/s", flops),
+            gemm: ("TFLOP/s", flops),
         },
-        "dominant": "gemm_blockscaled",
+        "dominant": gemm,
         "config": {"workload": f"dense Fprop projection X[{M}x{K}] bf16 1x128, W[{N}x{K}] bf16 128x128, "
-                               f"C[{M}x{N}] bf16", "M": M, "N": N, "K": K, "input_rotations": R},
+                               f"{out}", "M": M, "N": N, "K": K, "input_rotations": R},
     }
     return step, info
+
+
+def setup_fprop_q1x128(torch, fb, dev):
+    return setup_dense_fprop(torch, fb, dev, fused=True)
 
 
 def setup_backward(torch, fb, dev, M=4096, N=7168, K=7168):
@@ -322,8 +342,8 @@ def setup_copy(torch, fb, dev, nbytes=None):
     return step, info
 
 
-WORKLOADS = {"copy": setup_copy, "dense_fprop": setup_dense_fprop, "backward": setup_backward, "moe": setup_moe,
-             "decode": setup_decode}
+WORKLOADS = {"copy": setup_copy, "dense_fprop": setup_dense_fprop, "fprop_q1x128": setup_fprop_q1x128,
+             "backward": setup_backward, "moe": setup_moe, "decode": setup_decode}
 
 
 # ---------------------------------------------------------------------------
@@ -359,13 +379,17 @@ def cpu_baseline(workload):
     M, N, K = 1024, 4096, 7168
     X = torch.randn(M, K, generator=g).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     W = (torch.randn(N, K, generator=g) * 0.006).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    fused = workload == "fprop_q1x128"
     t0 = time.perf_counter()
     qx, sx = oracle.quant_act_1x128(X)
     qw, sw = oracle.quant_w_128x128(W)
-    oracle.gemm_ref(qx, sx, qw, sw)
+    C, _ = oracle.gemm_ref(qx, sx, qw, sw)
+    if fused:
+        oracle.quant_act_1x128(C.astype(np.float32))
     dt = time.perf_counter() - t0
+    what = "GEMM, quantize C 1x128" if fused else "GEMM"
     return {"value": 2.0 * M * N * K / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"one Fprop step at {M}x{N}x{K}: quantize X 1x128 and W 128x128, GEMM; {dt:.1f} s"}
+            "sample": f"one Fprop step at {M}x{N}x{K}: quantize X 1x128 and W 128x128, {what}; {dt:.1f} s"}
 
 
 def main():

@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libfp8bs.so")
 
 F32, BF16 = 0, 1
 SCALE_BLOCK128, SCALE_ROW = 0, 1
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 _c_int64 = ctypes.c_int64
 _vp = ctypes.c_void_p
@@ -27,6 +27,8 @@ _SIGNATURES = {
     "fp8_quant_w_128x128": [_vp, ctypes.c_int, _c_int64, _c_int64, _vp, _vp, _vp, _vp, _vp],
     "fp8_quant_act_128x1_T": [_vp, ctypes.c_int, _c_int64, _c_int64, _vp, _vp, _vp],
     "fp8_gemm_blockscaled": [_vp, _vp, _vp, _vp, ctypes.c_int, _vp, _c_int64, _c_int64, _c_int64, _vp],
+    "fp8_gemm_blockscaled_q1x128": [_vp, _vp, _vp, _vp, ctypes.c_int, _vp, _vp, _c_int64, _c_int64,
+                                    _c_int64, _vp],
     "fp8_grouped_gemm_blockscaled": [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _c_int64, _c_int64,
                                      _c_int64, _vp],
     "fp8bs_status_string": [ctypes.c_int],
@@ -133,8 +135,8 @@ def fp8_quant_act_128x1_T(x):
     return qT, sT
 
 
-def fp8_gemm_blockscaled(A, sA, B, sB, b_scale_mode=SCALE_BLOCK128, out=None):
-    """C[M][N] (bf16) = block-scaled FP8 GEMM of A[M][K] and B[N][K] (both K-contiguous)."""
+def _gemm_operands(A, sA, B, sB, b_scale_mode):
+    """(M, N, K, pointers) of a dense GEMM's operands after the shape checks."""
     M, K = A.shape
     N = B.shape[0]
     if B.shape[1] != K:
@@ -147,10 +149,14 @@ def fp8_gemm_blockscaled(A, sA, B, sB, b_scale_mode=SCALE_BLOCK128, out=None):
         raise ValueError("unknown b_scale_mode")
     if tuple(sA.shape) != (K // 128, M) or tuple(sB.shape) != exp_sb:
         raise ValueError(f"scale grids {tuple(sA.shape)}, {tuple(sB.shape)} do not match the operands")
-    pa = _dev(A, "A", (torch.uint8,))
-    psa = _dev(sA, "sA", (torch.float32,))
-    pb = _dev(B, "B", (torch.uint8,))
-    psb = _dev(sB, "sB", (torch.float32,))
+    ptrs = (_dev(A, "A", (torch.uint8,)), _dev(sA, "sA", (torch.float32,)),
+            _dev(B, "B", (torch.uint8,)), _dev(sB, "sB", (torch.float32,)))
+    return M, N, K, ptrs
+
+
+def fp8_gemm_blockscaled(A, sA, B, sB, b_scale_mode=SCALE_BLOCK128, out=None):
+    """C[M][N] (bf16) = block-scaled FP8 GEMM of A[M][K] and B[N][K] (both K-contiguous)."""
+    M, N, K, (pa, psa, pb, psb) = _gemm_operands(A, sA, B, sB, b_scale_mode)
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
     pc = _dev(out, "out", (torch.bfloat16,))
@@ -159,6 +165,17 @@ def fp8_gemm_blockscaled(A, sA, B, sB, b_scale_mode=SCALE_BLOCK128, out=None):
     _check("fp8_gemm_blockscaled",
            lib().fp8_gemm_blockscaled(pa, psa, pb, psb, int(b_scale_mode), pc, M, N, K, _stream(A)))
     return out
+
+
+def fp8_gemm_blockscaled_q1x128(A, sA, B, sB, b_scale_mode=SCALE_BLOCK128):
+    """The GEMM's BF16 result quantized 1x128: (Q uint8 [M][N], sQ float32 [N/128][M])."""
+    M, N, K, (pa, psa, pb, psb) = _gemm_operands(A, sA, B, sB, b_scale_mode)
+    Q = torch.empty((M, N), dtype=torch.uint8, device=A.device)
+    sQ = torch.empty((N // 128, M), dtype=torch.float32, device=A.device)
+    _check("fp8_gemm_blockscaled_q1x128",
+           lib().fp8_gemm_blockscaled_q1x128(pa, psa, pb, psb, int(b_scale_mode), Q.data_ptr(),
+                                             sQ.data_ptr(), M, N, K, _stream(A)))
+    return Q, sQ
 
 
 def fp8_grouped_gemm_blockscaled(A, sA, B, sB, group_offsets, out=None):

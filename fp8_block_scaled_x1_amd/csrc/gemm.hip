@@ -168,7 +168,9 @@ struct Tile {
   int sa_stride;
   const uint8_t* B;   // this tile's B, [N][K]
   const float* sB;    // block: [N/128][K/128]; row: [K/128][N]
-  uint16_t* C;        // [rows][N]
+  uint16_t* C;        // [rows][N] (BF16 output)
+  uint8_t* Q;         // [rows][N] (quantized output: E4M3 codes)
+  float* sQ;          // [N/128][rows] (quantized output: 1x128 group scales)
   int m0, row_end;    // tile rows m0 .. m0+BM-1, valid below row_end
   int n0, N, K;
 };
@@ -181,7 +183,10 @@ template <int N>
 __device__ __forceinline__ void wait_and_barrier() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
-template <class G, int ROW_MODE>
+// QOUT: the epilogue writes the 1x128 quantization (E4M3 codes and FP32
+// scales per row and 128 columns) of the BF16-rounded result instead of the
+// BF16 result itself.
+template <class G, int ROW_MODE, int QOUT = 0>
 __device__ __forceinline__ void run_tile(const Tile& t, uint8_t* smem) {
   constexpr int MS = G::MS, NS = G::NS, WM = G::WM, WN = G::WN;
   constexpr bool kDeepA = G::DA == 3, kDeepB = G::DB == 3, kDeep = kDeepA || kDeepB;
@@ -504,31 +509,90 @@ __device__ __forceinline__ void run_tile(const Tile& t, uint8_t* smem) {
     }
   }
 
-  // BF16 epilogue, round to nearest even: lane holds C[m][n..n+3]
+  // lane holds C[m][n..n+3] of every MFMA tile
   const int m_lane = t.m0 + wm * WM + (lane & 15);
   const int n_lane = t.n0 + wn * WN + 4 * (lane >> 4);
+  if constexpr (!QOUT) {
+    // BF16 epilogue, round to nearest even
 #pragma unroll
-  for (int i = 0; i < MS; ++i) {
-    const int m = m_lane + 16 * i;
-    if (m >= t.row_end) continue;
+    for (int i = 0; i < MS; ++i) {
+      const int m = m_lane + 16 * i;
+      if (m >= t.row_end) continue;
 #pragma unroll
-    for (int j = 0; j < NS; ++j) {
-      const int n = n_lane + 16 * j;
-      if (n >= t.N) continue;
-      uint2 o;
-      o.x = float_to_bf16_bits(acc[i][j][0]) | (float_to_bf16_bits(acc[i][j][1]) << 16);
-      o.y = float_to_bf16_bits(acc[i][j][2]) | (float_to_bf16_bits(acc[i][j][3]) << 16);
-      *reinterpret_cast<uint2*>(t.C + (int64_t)m * t.N + n) = o;
+      for (int j = 0; j < NS; ++j) {
+        const int n = n_lane + 16 * j;
+        if (n >= t.N) continue;
+        uint2 o;
+        o.x = float_to_bf16_bits(acc[i][j][0]) | (float_to_bf16_bits(acc[i][j][1]) << 16);
+        o.y = float_to_bf16_bits(acc[i][j][2]) | (float_to_bf16_bits(acc[i][j][3]) << 16);
+        *reinterpret_cast<uint2*>(t.C + (int64_t)m * t.N + n) = o;
+      }
+    }
+  } else {
+    // Quantizing epilogue: the 1x128 quantizer applied to the BF16-rounded
+    // result, fused. A 128-column group spans kGW = 128 / WN waves along n;
+    // each row's amax is reduced over the lane's values, the four lanes that
+    // share the row (xor 16, xor 32) and, through LDS, the group's waves.
+    static_assert(G::BN % kGroup == 0 && kGroup % WN == 0, "tile columns must hold whole 128-column groups");
+    constexpr int kGW = kGroup / WN;
+    float v[MS][NS][4];
+    float ra[MS];
+#pragma unroll
+    for (int i = 0; i < MS; ++i) {
+      float a = 0.0f;
+#pragma unroll
+      for (int j = 0; j < NS; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          v[i][j][r] = __uint_as_float(float_to_bf16_bits(acc[i][j][r]) << 16);
+          a = fmaxf(a, fabsf(v[i][j][r]));
+        }
+      a = fmaxf(a, __shfl_xor(a, 16, 64));
+      a = fmaxf(a, __shfl_xor(a, 32, 64));
+      ra[i] = a;
+    }
+    if constexpr (kGW > 1) {
+      // red[wave][row of the wave's subtile]: every wave's row maxima, after
+      // all waves are done with the operand slots
+      float* red = reinterpret_cast<float*>(smem);
+      wait_and_barrier<0>();
+      if (lane < 16) {
+#pragma unroll
+        for (int i = 0; i < MS; ++i) red[wave * WM + 16 * i + lane] = ra[i];
+      }
+      wait_and_barrier<0>();
+      const int wn0 = wn - wn % kGW;
+#pragma unroll
+      for (int i = 0; i < MS; ++i)
+#pragma unroll
+        for (int w2 = 0; w2 < kGW; ++w2)
+          ra[i] = fmaxf(ra[i], red[(wm * G::WGN + wn0 + w2) * WM + 16 * i + (lane & 15)]);
+    }
+    const int grp = (t.n0 + wn * WN) / kGroup;
+    const bool group_ok = t.n0 + wn * WN < t.N;   // N % 128 == 0: a group is wholly in or out
+#pragma unroll
+    for (int i = 0; i < MS; ++i) {
+      const int m = m_lane + 16 * i;
+      const GroupDiv g = group_div<true>(ra[i]);   // the values are BF16 numbers
+      if (m < t.row_end && group_ok) {
+#pragma unroll
+        for (int j = 0; j < NS; ++j)
+          *reinterpret_cast<uint32_t*>(t.Q + (int64_t)m * t.N + n_lane + 16 * j) =
+              e4m3_div_pack4_t<true>(v[i][j][0], v[i][j][1], v[i][j][2], v[i][j][3], g);
+        if (lane < 16 && wn % kGW == 0) t.sQ[(int64_t)grp * t.row_end + m] = g.s;
+      }
     }
   }
 }
 
-template <class G, int ROW_MODE>
+template <class G, int ROW_MODE, int QOUT>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const uint8_t* __restrict__ A,
                                                             const float* __restrict__ sA,
                                                             const uint8_t* __restrict__ B,
                                                             const float* __restrict__ sB,
-                                                            uint16_t* __restrict__ C, int M, int N,
+                                                            uint16_t* __restrict__ C,
+                                                            uint8_t* __restrict__ Q,
+                                                            float* __restrict__ sQ, int M, int N,
                                                             int K) {
   __shared__ __align__(16) uint8_t smem[G::kLdsBytes];
   const int tiles_m = (M + G::BM - 1) / G::BM, tiles_n = (N + G::BN - 1) / G::BN;
@@ -537,10 +601,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const uint8_t* __rest
   tile_coords(pid, tiles_m, tiles_n, tm, tn);
   Tile t;
   t.A = A; t.sA = sA; t.sa_stride = M;
-  t.B = B; t.sB = sB; t.C = C;
+  t.B = B; t.sB = sB; t.C = C; t.Q = Q; t.sQ = sQ;
   t.m0 = tm * G::BM; t.row_end = M;
   t.n0 = tn * G::BN; t.N = N; t.K = K;
-  run_tile<G, ROW_MODE>(t, smem);
+  run_tile<G, ROW_MODE, QOUT>(t, smem);
 }
 
 // Per-expert tiles: expert e owns rows [off[e], off[e+1]); its tiles are
@@ -597,7 +661,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
   t.A = A; t.sA = sA; t.sa_stride = M_total;
   t.B = B + (int64_t)e_found * N * K;
   t.sB = sB + (int64_t)e_found * (N / BK) * nkb;
-  t.C = C;
+  t.C = C; t.Q = nullptr; t.sQ = nullptr;
   t.m0 = r0 + tm * G::BM; t.row_end = r1;
   t.n0 = tn * G::BN; t.N = N; t.K = K;
   run_tile<G, 0>(t, smem);
@@ -634,17 +698,17 @@ int pick_dense(int64_t M, int64_t N) {
   return c1 <= c2 ? 1 : 2;
 }
 
-template <class G>
+template <class G, int QOUT>
 hipError_t launch_dense(const uint8_t* A, const float* sA, const uint8_t* B, const float* sB,
-                        int row_mode, uint16_t* C, int64_t M, int64_t N, int64_t K,
-                        hipStream_t stream) {
+                        int row_mode, uint16_t* C, uint8_t* Q, float* sQ, int64_t M, int64_t N,
+                        int64_t K, hipStream_t stream) {
   const int tiles = (int)(((M + G::BM - 1) / G::BM) * ((N + G::BN - 1) / G::BN));
   if (row_mode)
-    hipLaunchKernelGGL((gemm_kernel<G, 1>), dim3(tiles), dim3(kThreads), 0, stream, A, sA, B, sB, C,
-                       (int)M, (int)N, (int)K);
+    hipLaunchKernelGGL((gemm_kernel<G, 1, QOUT>), dim3(tiles), dim3(kThreads), 0, stream, A, sA, B, sB,
+                       C, Q, sQ, (int)M, (int)N, (int)K);
   else
-    hipLaunchKernelGGL((gemm_kernel<G, 0>), dim3(tiles), dim3(kThreads), 0, stream, A, sA, B, sB, C,
-                       (int)M, (int)N, (int)K);
+    hipLaunchKernelGGL((gemm_kernel<G, 0, QOUT>), dim3(tiles), dim3(kThreads), 0, stream, A, sA, B, sB,
+                       C, Q, sQ, (int)M, (int)N, (int)K);
   return hipGetLastError();
 }
 
@@ -655,10 +719,23 @@ hipError_t launch_gemm_blockscaled(const uint8_t* A, const float* sA, const uint
                                    int64_t N, int64_t K, hipStream_t stream) {
   using namespace gemm;
   switch (pick_dense(M, N)) {
-    case 1: return launch_dense<Cfg256x224>(A, sA, B, sB, row_mode, C, M, N, K, stream);
-    case 2: return launch_dense<Cfg224x256>(A, sA, B, sB, row_mode, C, M, N, K, stream);
-    default: return launch_dense<Cfg256x256>(A, sA, B, sB, row_mode, C, M, N, K, stream);
+    case 1: return launch_dense<Cfg256x224, 0>(A, sA, B, sB, row_mode, C, nullptr, nullptr, M, N, K, stream);
+    case 2: return launch_dense<Cfg224x256, 0>(A, sA, B, sB, row_mode, C, nullptr, nullptr, M, N, K, stream);
+    default: return launch_dense<Cfg256x256, 0>(A, sA, B, sB, row_mode, C, nullptr, nullptr, M, N, K, stream);
   }
+}
+
+hipError_t launch_gemm_blockscaled_q1x128(const uint8_t* A, const float* sA, const uint8_t* B,
+                                          const float* sB, int row_mode, uint8_t* Q, float* sQ,
+                                          int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+  using namespace gemm;
+  // tiles whose columns hold whole 128-column groups: 256x256 or 224x256
+  const int cus = device_cus();
+  const int64_t tn = (N + 255) / 256;
+  const int64_t c0 = round_cost<Cfg256x256>(((M + 255) / 256) * tn, cus);
+  const int64_t c2 = round_cost<Cfg224x256>(((M + 223) / 224) * tn, cus);
+  if (c2 < c0) return launch_dense<Cfg224x256, 1>(A, sA, B, sB, row_mode, nullptr, Q, sQ, M, N, K, stream);
+  return launch_dense<Cfg256x256, 1>(A, sA, B, sB, row_mode, nullptr, Q, sQ, M, N, K, stream);
 }
 
 hipError_t launch_grouped_gemm_blockscaled(const uint8_t* A, const float* sA, const uint8_t* B,

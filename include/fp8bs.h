@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define FP8BS_ABI_VERSION 1
+#define FP8BS_ABI_VERSION 2
 
 #ifndef FP8BS_API
 #define FP8BS_API __attribute__((visibility("default")))
@@ -127,6 +127,23 @@ FP8BS_API int fp8_quant_act_128x1_T(const void* x, int dtype, int64_t M, int64_t
  */
 FP8BS_API int fp8_gemm_blockscaled(const uint8_t* A, const float* sA, const uint8_t* B,
                          const float* sB, int b_scale_mode, uint16_t* C,
+                         int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
+ * The same GEMM with a quantizing epilogue: instead of the BF16 result it
+ * writes that result's 1x128 quantization, the FP8 codes and FP32 scales the
+ * next layer's GEMM reads (report section 3.5.2 on the innerforce.co.kr page:
+ * FP8 conversion fused with the movement of activations). Q and sQ are
+ * exactly what fp8_quant_act_1x128 (BF16 input) would produce from the C that
+ * fp8_gemm_blockscaled writes, so C never goes to memory.
+ *   A, sA, B, sB, b_scale_mode  as for fp8_gemm_blockscaled
+ *   Q   [M][N]      uint8 E4M3 codes
+ *   sQ  [N/128][M]  float32, sQ[g][m] = amax(C[m][128g .. 128g+127]) / 448,
+ *                   1.0 for a zero group
+ * Shapes, sizes, ownership and errors as for fp8_gemm_blockscaled.
+ */
+FP8BS_API int fp8_gemm_blockscaled_q1x128(const uint8_t* A, const float* sA, const uint8_t* B,
+                         const float* sB, int b_scale_mode, uint8_t* Q, float* sQ,
                          int64_t M, int64_t N, int64_t K, void* stream);
 
 /*
