@@ -6,9 +6,10 @@ default workload is the dense Fprop projection (X[4096][7168] BF16 quantized
 1x128, W[7168][7168] BF16 quantized 128x128, block-scaled FP8 GEMM with FP32
 promotion per 128-wide K chunk, BF16 output). Other workloads (--workload)
 measure the remaining forms of the path: the backward pair (Dgrad + Wgrad with
-the 128x1 transposed quantizer), the grouped MoE expert GEMMs, the
-decode-shaped grouped GEMM, and the Fprop whose GEMM writes the next layer's
-1x128-quantized input directly (fused quantizing epilogue).
+the 128x1 transposed quantizer), the grouped MoE expert GEMMs and their
+backward (grouped Dgrad, grouped 128x1 transposed quantizers, per-expert
+Wgrad), the decode-shaped grouped GEMM, and the Fprop whose GEMM writes the
+next layer's 1x128-quantized input directly (fused quantizing epilogue).
 
 Prints one JSON line. `value` is whole-step throughput with inputs resident in
 HBM; `roofline` describes the dominant kernel, timed live with HIP events on
@@ -286,6 +287,90 @@ def setup_moe(torch, fb, dev):
     return step, info
 
 
+def setup_moe_backward(torch, fb, dev):
+    """Backward of the grouped expert GEMMs, down then up: per projection the
+    1x128 quantizer of dY and the grouped Dgrad on the weights' transposed
+    copies, then the grouped 128x1 transposed quantizers of dY and of the
+    forward input, and the per-expert Wgrad."""
+    import workloads
+    d = workloads.grouped_moe_backward(device=dev)
+    off = torch.from_numpy(d["offsets"]).to(dev)
+    Mt = int(d["offsets"][-1])
+    E = len(d["counts"])
+    ld = fb.grouped_ld(Mt, E)
+    L = fb.lib()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    proj = []
+    for tag, dy_key, x_key, w_key in (("down", "dY_dn", "A_dn", "W_dn"), ("up", "dY_up", "A_up", "W_up")):
+        W = d.pop(w_key)
+        _, N, K = W.shape        # forward: C[M][N] = X[M][K] W^T
+        qwT = torch.empty((E, K, N), dtype=torch.uint8, device=dev)
+        swT = torch.empty((E, K // 128, N // 128), dtype=torch.float32, device=dev)
+        for e in range(E):
+            _, _, qwT[e], swT[e] = fb.fp8_quant_w_128x128(W[e], transposed=True)   # quantized in the forward pass
+        del W
+        proj.append({
+            "tag": tag, "N": N, "K": K, "dY": d[dy_key], "X": d[x_key], "qwT": qwT, "swT": swT,
+            "qdy": torch.empty((Mt, N), dtype=torch.uint8, device=dev),
+            "sdy": torch.empty((N // 128, Mt), dtype=torch.float32, device=dev),
+            "dX": torch.empty((Mt, K), dtype=torch.bfloat16, device=dev),
+            "qdyT": torch.empty((N, ld), dtype=torch.uint8, device=dev),
+            "sdyT": torch.empty((ld // 128, N), dtype=torch.float32, device=dev),
+            "qxT": torch.empty((K, ld), dtype=torch.uint8, device=dev),
+            "sxT": torch.empty((ld // 128, K), dtype=torch.float32, device=dev),
+            "dW": torch.empty((E, N, K), dtype=torch.bfloat16, device=dev),
+        })
+    torch.cuda.empty_cache()
+
+    def step(timer):
+        rc = 0
+        timer.mark()
+        for p in proj:
+            N, K = p["N"], p["K"]
+            rc |= L.fp8_quant_act_1x128(p["dY"].data_ptr(), fb.BF16, Mt, N, p["qdy"].data_ptr(), p["sdy"].data_ptr(),
+                                        stream)
+            timer.mark()
+            rc |= L.fp8_grouped_gemm_blockscaled(p["qdy"].data_ptr(), p["sdy"].data_ptr(), p["qwT"].data_ptr(),
+                                                 p["swT"].data_ptr(), p["dX"].data_ptr(), off.data_ptr(), E, Mt, K, N,
+                                                 stream)
+            timer.mark()
+            rc |= L.fp8_quant_act_128x1_T_grouped(p["dY"].data_ptr(), fb.BF16, Mt, N, off.data_ptr(), E, ld,
+                                                  p["qdyT"].data_ptr(), p["sdyT"].data_ptr(), stream)
+            timer.mark()
+            rc |= L.fp8_quant_act_128x1_T_grouped(p["X"].data_ptr(), fb.BF16, Mt, K, off.data_ptr(), E, ld,
+                                                  p["qxT"].data_ptr(), p["sxT"].data_ptr(), stream)
+            timer.mark()
+            rc |= L.fp8_grouped_gemm_wgrad(p["qdyT"].data_ptr(), p["sdyT"].data_ptr(), p["qxT"].data_ptr(),
+                                           p["sxT"].data_ptr(), p["dW"].data_ptr(), off.data_ptr(), E, Mt, N, K, ld,
+                                           stream)
+            timer.mark()
+        if rc:
+            raise RuntimeError(f"libfp8bs call failed ({rc})")
+
+    names, work, flops = [], {}, 0.0
+    for p in proj:
+        N, K, t = p["N"], p["K"], p["tag"]
+        f = 2.0 * Mt * N * K
+        for n, w in ((f"quant_act_1x128(dY_{t})", ("GB/s", Mt * N * 3 + Mt * N // 32)),
+                     (f"grouped_dgrad_{t}", ("TFLOP/s", f)),
+                     (f"quant_128x1_T_grouped(dY_{t})", ("GB/s", Mt * N * 3 + Mt * N // 32)),
+                     (f"quant_128x1_T_grouped(X_{t})", ("GB/s", Mt * K * 3 + Mt * K // 32)),
+                     (f"grouped_wgrad_{t}", ("TFLOP/s", f))):
+            names.append(n)
+            work[n] = w
+        flops += 2 * f
+    info = {
+        "names": names,
+        "step_flops": flops,
+        "work": work,
+        "dominant": "grouped_wgrad_up",
+        "config": {"workload": f"grouped MoE backward: {E} experts, {Mt} routed rows (8192 tokens x top-8, "
+                               f"Dirichlet(0.5)); down (dX 7168->2048, dW 7168x2048) then up (dX 4096->7168, "
+                               f"dW 4096x7168) per expert", "E": E, "rows": Mt, "ld": ld},
+    }
+    return step, info
+
+
 def setup_decode(torch, fb, dev):
     """Decode-shaped grouped GEMM: 32 experts, 1..256 rows each, weights pre-quantized."""
     import workloads
@@ -343,7 +428,8 @@ def setup_copy(torch, fb, dev, nbytes=None):
 
 
 WORKLOADS = {"copy": setup_copy, "dense_fprop": setup_dense_fprop, "fprop_q1x128": setup_fprop_q1x128,
-             "backward": setup_backward, "moe": setup_moe, "decode": setup_decode}
+             "backward": setup_backward, "moe": setup_moe, "moe_backward": setup_moe_backward,
+             "decode": setup_decode}
 
 
 # ---------------------------------------------------------------------------
@@ -376,6 +462,20 @@ def cpu_baseline(workload):
         nbytes = N * K + M * K + M * N * 2
         return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
                 "sample": f"one decode expert: GEMM {M}x{N}x{K} (pre-quantized operands), {dt:.1f} s"}
+    if workload == "moe_backward":
+        # one expert's Wgrad: 1000 tokens (8 groups, the last one padded), dW 4096 x 7168
+        T, N, K = 1000, 4096, 7168
+        dY = (torch.randn(T, N, generator=g) * 1e-3).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        X = torch.randn(T, K, generator=g).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        off = np.array([0, T])
+        t0 = time.perf_counter()
+        qa, sa = oracle.quant_act_128x1_T_grouped(dY, off)
+        qb, sb = oracle.quant_act_128x1_T_grouped(X, off)
+        oracle.grouped_wgrad_ref(qa, sa, qb, sb, off)
+        dt = time.perf_counter() - t0
+        return {"value": 2.0 * T * N * K / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+                "sample": f"one expert's Wgrad over {T} tokens: grouped 128x1 quantizers of dY[{T}x{N}] and "
+                          f"X[{T}x{K}], per-expert Wgrad GEMM; {dt:.1f} s"}
     M, N, K = 1024, 4096, 7168
     X = torch.randn(M, K, generator=g).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     W = (torch.randn(N, K, generator=g) * 0.006).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)

@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libfp8bs.so")
 
 F32, BF16 = 0, 1
 SCALE_BLOCK128, SCALE_ROW = 0, 1
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 _c_int64 = ctypes.c_int64
 _vp = ctypes.c_void_p
@@ -31,6 +31,10 @@ _SIGNATURES = {
                                     _c_int64, _vp],
     "fp8_grouped_gemm_blockscaled": [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _c_int64, _c_int64,
                                      _c_int64, _vp],
+    "fp8_quant_act_128x1_T_grouped": [_vp, ctypes.c_int, _c_int64, _c_int64, _vp, ctypes.c_int, _c_int64, _vp,
+                                      _vp, _vp],
+    "fp8_grouped_gemm_wgrad": [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _c_int64, _c_int64, _c_int64,
+                               _c_int64, _vp],
     "fp8bs_status_string": [ctypes.c_int],
     "fp8bs_abi_version": [],
 }
@@ -198,4 +202,59 @@ def fp8_grouped_gemm_blockscaled(A, sA, B, sB, group_offsets, out=None):
     pc = _dev(out, "out", (torch.bfloat16,))
     _check("fp8_grouped_gemm_blockscaled",
            lib().fp8_grouped_gemm_blockscaled(pa, psa, pb, psb, pc, po, E, M_total, N, K, _stream(A)))
+    return out
+
+
+def grouped_ld(M_total, E):
+    """Smallest valid row length of the grouped 128x1 transposed codes:
+    room for M_total tokens plus every expert's padding, in whole groups."""
+    return 128 * ((M_total + 127 * E + 127) // 128)
+
+
+def fp8_quant_act_128x1_T_grouped(x, group_offsets, ld=None):
+    """x[M_total][C] rows grouped by expert -> (qT uint8 [C][ld], sT float32 [ld/128][C]).
+
+    Expert e's tokens are cut into groups of 128 from its first row (the last
+    one zero-padded); groups are numbered expert-major. Columns and scale rows
+    past the last group are left as allocated (uninitialized).
+    """
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D")
+    M, C = x.shape
+    E = group_offsets.shape[0] - 1
+    if E < 0:
+        raise ValueError("group_offsets must have E+1 entries")
+    ld = grouped_ld(M, E) if ld is None else int(ld)
+    px = _dev(x, "x", (torch.float32, torch.bfloat16))
+    po = _dev(group_offsets, "group_offsets", (torch.int32,))
+    qT = torch.empty((C, ld), dtype=torch.uint8, device=x.device)
+    sT = torch.empty((ld // 128, C), dtype=torch.float32, device=x.device)
+    _check("fp8_quant_act_128x1_T_grouped",
+           lib().fp8_quant_act_128x1_T_grouped(px, _in_dtype(x), M, C, po, E, ld, qT.data_ptr(), sT.data_ptr(),
+                                               _stream(x)))
+    return qT, sT
+
+
+def fp8_grouped_gemm_wgrad(A, sA, B, sB, group_offsets, M_total, out=None):
+    """Per-expert Wgrad: C[e] = dY_e^T X_e from the grouped 128x1 transposed
+    quantizations A = qT(dY) [N][ld], B = qT(X) [K][ld]; returns bf16 [E][N][K]."""
+    N, ld = A.shape
+    K, ldb = B.shape
+    E = group_offsets.shape[0] - 1
+    if ldb != ld:
+        raise ValueError("A and B disagree on the token length")
+    if tuple(sA.shape) != (ld // 128, N) or tuple(sB.shape) != (ld // 128, K):
+        raise ValueError("scale grids do not match the operands")
+    pa = _dev(A, "A", (torch.uint8,))
+    psa = _dev(sA, "sA", (torch.float32,))
+    pb = _dev(B, "B", (torch.uint8,))
+    psb = _dev(sB, "sB", (torch.float32,))
+    po = _dev(group_offsets, "group_offsets", (torch.int32,))
+    if out is None:
+        out = torch.empty((E, N, K), dtype=torch.bfloat16, device=A.device)
+    pc = _dev(out, "out", (torch.bfloat16,))
+    if tuple(out.shape) != (E, N, K):
+        raise ValueError("out has the wrong shape")
+    _check("fp8_grouped_gemm_wgrad",
+           lib().fp8_grouped_gemm_wgrad(pa, psa, pb, psb, pc, po, E, int(M_total), N, K, ld, _stream(A)))
     return out

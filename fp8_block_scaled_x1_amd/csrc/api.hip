@@ -124,4 +124,36 @@ int fp8_grouped_gemm_blockscaled(const uint8_t* A, const float* sA, const uint8_
                                                           M_total, N, K, as_stream(stream)));
 }
 
+int fp8_quant_act_128x1_T_grouped(const void* x, int dtype, int64_t M_total, int64_t C,
+                                  const int32_t* group_offsets, int E, int64_t ld, uint8_t* qT,
+                                  float* sT, void* stream) {
+  if (!valid_dtype(dtype)) return FP8BS_ERR_DTYPE;
+  if (E < 0 || M_total < 0 || C < 0 || C % kG || ld < 0 || ld % kG) return FP8BS_ERR_SHAPE;
+  if (E == 0 && M_total > 0) return FP8BS_ERR_SHAPE;     // rows with no expert
+  if (ld < M_total + (kG - 1) * E) return FP8BS_ERR_SHAPE;
+  if (M_total >= kI32 || C >= kI32 || ld / kG > 65535) return FP8BS_ERR_TOO_LARGE;
+  if (M_total == 0 || C == 0) return FP8BS_OK;
+  if (!x || !qT || !sT || !group_offsets) return FP8BS_ERR_NULL_PTR;
+  if (misaligned(x) || misaligned(qT) || misaligned(sT)) return FP8BS_ERR_ALIGN;
+  return status_of(fp8bs::launch_quant_act_128x1_T_grouped(x, dtype == FP8BS_BF16, M_total, C, group_offsets,
+                                                           E, ld, qT, sT, as_stream(stream)));
+}
+
+int fp8_grouped_gemm_wgrad(const uint8_t* A, const float* sA, const uint8_t* B, const float* sB,
+                           uint16_t* C, const int32_t* group_offsets, int E, int64_t M_total,
+                           int64_t N, int64_t K, int64_t ld, void* stream) {
+  if (E < 0 || M_total < 0 || N < 0 || K < 0 || N % kG || K % kG || ld < 0 || ld % kG)
+    return FP8BS_ERR_SHAPE;
+  if (E == 0 && M_total > 0) return FP8BS_ERR_SHAPE;
+  if (ld < M_total + (kG - 1) * E) return FP8BS_ERR_SHAPE;
+  if (M_total >= kI32 || N * ld >= kI32 || K * ld >= kI32 || (int64_t)E * (N / kG) * (K / kG) >= kI32)
+    return FP8BS_ERR_TOO_LARGE;
+  if (E == 0 || N == 0 || K == 0) return FP8BS_OK;
+  if (!A || !sA || !B || !sB || !C || !group_offsets) return FP8BS_ERR_NULL_PTR;
+  if (misaligned(A) || misaligned(sA) || misaligned(B) || misaligned(sB) || misaligned(C))
+    return FP8BS_ERR_ALIGN;
+  return status_of(fp8bs::launch_grouped_gemm_wgrad(A, sA, B, sB, C, group_offsets, E, M_total, N, K, ld,
+                                                    as_stream(stream)));
+}
+
 }  // extern "C"

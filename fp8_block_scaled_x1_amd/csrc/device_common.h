@@ -209,4 +209,81 @@ __device__ __forceinline__ uint32_t pack4(uint32_t c0, uint32_t c1, uint32_t c2,
   return c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
 }
 
+// ---------------------------------------------------------------------------
+// Per-expert work lists. Expert e owns rows [a_e, b_e) with
+// a_e = clamp(off[e], 0, M_total) and b_e = clamp(off[e+1], a_e, M_total);
+// it has units(e) = ceil((b_e - a_e) / unit_rows) * mult work units, numbered
+// expert-major. Lane l of the calling wave examines expert e0 + l of each
+// batch of 64 (the offsets of a batch are read at once) and a prefix sum over
+// the lanes finds the answer; every result is wave-uniform.
+// ---------------------------------------------------------------------------
+struct ExpertSlot {
+  int e;        // expert of the unit, -1 if the unit is past the last
+  int r0, r1;   // its row range
+  int base;     // units of the experts before it
+};
+
+__device__ __forceinline__ ExpertSlot locate_expert(const int32_t* __restrict__ off, int E, int M_total,
+                                                    int unit, int unit_rows, int mult) {
+  const int lane = threadIdx.x & 63;
+  ExpertSlot r{-1, 0, 0, 0};
+  int base = 0;
+  for (int e0 = 0; e0 < E; e0 += 64) {
+    const int e = e0 + lane;
+    int a = 0, b = 0, ue = 0;
+    if (e < E) {
+      a = min(max(off[e], 0), M_total);
+      b = min(max(off[e + 1], a), M_total);
+      ue = ((b - a + unit_rows - 1) / unit_rows) * mult;
+    }
+    int incl = ue;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int v = __shfl_up(incl, d, 64);
+      if (lane >= d) incl += v;
+    }
+    const uint64_t hit = __ballot(e < E && unit < base + incl);
+    if (hit) {
+      const int l = __ffsll((unsigned long long)hit) - 1;
+      r.e = e0 + l;
+      r.r0 = __shfl(a, l, 64);
+      r.r1 = __shfl(b, l, 64);
+      base += __shfl(incl, l, 64) - __shfl(ue, l, 64);
+      break;
+    }
+    base += __shfl(incl, 63, 64);
+  }
+  r.e = __builtin_amdgcn_readfirstlane(r.e);
+  r.r0 = __builtin_amdgcn_readfirstlane(r.r0);
+  r.r1 = __builtin_amdgcn_readfirstlane(r.r1);
+  r.base = __builtin_amdgcn_readfirstlane(base);
+  return r;
+}
+
+// Units (as above, mult = 1) of the experts before expert e, with e's own
+// row range; wave-uniform.
+__device__ __forceinline__ ExpertSlot units_before(const int32_t* __restrict__ off, int M_total, int e,
+                                                   int unit_rows) {
+  const int lane = threadIdx.x & 63;
+  int sum = 0;
+  for (int e0 = 0; e0 < e; e0 += 64) {
+    const int x = e0 + lane;
+    if (x < e) {
+      const int a = min(max(off[x], 0), M_total);
+      const int b = min(max(off[x + 1], a), M_total);
+      sum += (b - a + unit_rows - 1) / unit_rows;
+    }
+  }
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) sum += __shfl_xor(sum, d, 64);
+  ExpertSlot r;
+  r.e = e;
+  r.r0 = min(max(off[e], 0), M_total);
+  r.r1 = min(max(off[e + 1], r.r0), M_total);
+  r.r0 = __builtin_amdgcn_readfirstlane(r.r0);
+  r.r1 = __builtin_amdgcn_readfirstlane(r.r1);
+  r.base = __builtin_amdgcn_readfirstlane(sum);
+  return r;
+}
+
 }  // namespace fp8bs

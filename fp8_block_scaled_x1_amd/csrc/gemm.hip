@@ -172,7 +172,8 @@ struct Tile {
   uint8_t* Q;         // [rows][N] (quantized output: E4M3 codes)
   float* sQ;          // [N/128][rows] (quantized output: 1x128 group scales)
   int m0, row_end;    // tile rows m0 .. m0+BM-1, valid below row_end
-  int n0, N, K;
+  int n0, N, K;       // K: inner length of this tile's product (a multiple of 128)
+  int ld;             // row stride of A and B in bytes (K for a plain GEMM)
 };
 
 // Wait until at most N of this wave's vector-memory operations are pending
@@ -210,7 +211,7 @@ __device__ __forceinline__ void run_tile(const Tile& t, uint8_t* smem) {
   auto slice_off = [&](int s, int first, int last) {
     const int rr = s * 8 + (lane >> 3);
     const uint32_t col = (uint32_t)(((lane & 7) ^ swz(rr)) << 4);
-    return (uint32_t)min(first + rr, last) * (uint32_t)t.K + col;
+    return (uint32_t)min(first + rr, last) * (uint32_t)t.ld + col;
   };
   constexpr int kAL = G::kASlicesPerWave, kBL = G::kBSlicesPerWave;
   uint32_t aoffs[kAL], boffs[kBL], alds[kAL], blds[kBL];
@@ -603,7 +604,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const uint8_t* __rest
   t.A = A; t.sA = sA; t.sa_stride = M;
   t.B = B; t.sB = sB; t.C = C; t.Q = Q; t.sQ = sQ;
   t.m0 = tm * G::BM; t.row_end = M;
-  t.n0 = tn * G::BN; t.N = N; t.K = K;
+  t.n0 = tn * G::BN; t.N = N; t.K = K; t.ld = K;
   run_tile<G, ROW_MODE, QOUT>(t, smem);
 }
 
@@ -618,42 +619,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
   __shared__ __align__(16) uint8_t smem[G::kLdsBytes];
   const int tiles_n = (N + G::BN - 1) / G::BN;
   const int pid = xcd_remap(blockIdx.x, gridDim.x);
-  // Find the expert of tile pid: lane l of every wave takes expert e0 + l of
-  // a batch of 64, counts its tiles, and a prefix sum over the lanes finds
-  // the first expert whose tiles reach past pid (all offsets of a batch are
-  // loaded at once, not one dependent load per expert).
-  const int lane = threadIdx.x & 63;
-  int base = 0, e_found = -1, r0 = 0, r1 = 0;
-  for (int e0 = 0; e0 < E; e0 += 64) {
-    const int e = e0 + lane;
-    int a = 0, b = 0, te = 0;
-    if (e < E) {
-      a = min(max(offsets[e], 0), M_total);
-      b = min(max(offsets[e + 1], a), M_total);
-      te = ((b - a + G::BM - 1) / G::BM) * tiles_n;
-    }
-    int incl = te;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int v = __shfl_up(incl, d, 64);
-      if (lane >= d) incl += v;
-    }
-    const uint64_t hit = __ballot(e < E && pid < base + incl);
-    if (hit) {
-      const int l = __ffsll((unsigned long long)hit) - 1;
-      e_found = e0 + l;
-      r0 = __shfl(a, l, 64);
-      r1 = __shfl(b, l, 64);
-      base += __shfl(incl, l, 64) - __shfl(te, l, 64);
-      break;
-    }
-    base += __shfl(incl, 63, 64);
-  }
-  e_found = __builtin_amdgcn_readfirstlane(e_found);
-  r0 = __builtin_amdgcn_readfirstlane(r0);
-  r1 = __builtin_amdgcn_readfirstlane(r1);
-  base = __builtin_amdgcn_readfirstlane(base);
-  if (e_found < 0) return;
+  // the expert of tile pid (tiles numbered expert-major)
+  const ExpertSlot es = locate_expert(offsets, E, M_total, pid, G::BM, tiles_n);
+  if (es.e < 0) return;
+  const int e_found = es.e, r0 = es.r0, r1 = es.r1, base = es.base;
   int tm, tn;
   tile_coords(pid - base, (r1 - r0 + G::BM - 1) / G::BM, tiles_n, tm, tn);
   const int64_t nkb = K / BK;
@@ -663,8 +632,57 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
   t.sB = sB + (int64_t)e_found * (N / BK) * nkb;
   t.C = C; t.Q = nullptr; t.sQ = nullptr;
   t.m0 = r0 + tm * G::BM; t.row_end = r1;
-  t.n0 = tn * G::BN; t.N = N; t.K = K;
+  t.n0 = tn * G::BN; t.N = N; t.K = K; t.ld = K;
   run_tile<G, 0>(t, smem);
+}
+
+// Per-expert Wgrad: C[e] = A_e B_e^T over expert e's tokens, row-mode scales.
+// A[N][ld] and B[K][ld] are the 128x1 transposed codes of the two operands
+// with every expert's tokens padded to whole 128-token groups: expert e's
+// groups are g = P_e .. P_e + ceil(rows_e / 128) - 1 with P_e the groups of
+// the experts before it, its tokens sit at columns 128 P_e .., and the scales
+// of group g are sA[g][*], sB[g][*]. Every expert has the same
+// ceil(N/BM) x ceil(K/BN) tiles; an expert without tokens gets zeros.
+//
+// A tile's cost is proportional to its expert's tokens, which vary widely, so
+// every expert's tiles are split evenly over the XCDs (workgroup b runs on XCD
+// b % 8): XCD x takes the x-th contiguous run of ceil(tiles / 8) tile indices
+// of each expert in turn (in the grouped tile order that run is a compact
+// block of m- and n-tiles, whose operand panels stay in that XCD's L2).
+template <class G>
+__global__ __launch_bounds__(kThreads, 1) void grouped_wgrad_kernel(
+    const uint8_t* __restrict__ A, const float* __restrict__ sA, const uint8_t* __restrict__ B,
+    const float* __restrict__ sB, uint16_t* __restrict__ C, const int32_t* __restrict__ offsets,
+    int M_total, int N, int K, int ld) {
+  __shared__ __align__(16) uint8_t smem[G::kLdsBytes];
+  const int tiles_m = (N + G::BM - 1) / G::BM, tiles_n = (K + G::BN - 1) / G::BN;
+  const int per_expert = tiles_m * tiles_n;
+  const int run = (per_expert + kXcds - 1) / kXcds;
+  const int xcd = blockIdx.x % kXcds, local = blockIdx.x / kXcds;
+  const int e = local / run;
+  const int idx = xcd * run + local % run;
+  if (idx >= per_expert) return;   // the last run of an expert may be short
+  int tm, tn;
+  tile_coords(idx, tiles_m, tiles_n, tm, tn);
+  const ExpertSlot es = units_before(offsets, M_total, e, BK);
+  // (with offsets that break the precondition, stay inside the ld / 128 groups)
+  const int groups = max(0, min((es.r1 - es.r0 + BK - 1) / BK, ld / BK - es.base));
+  uint16_t* Ce = C + (int64_t)e * N * K;
+  if (groups == 0) {
+    // no tokens: a zero tile (whole 8-byte pieces; K % 128 == 0)
+    for (int p = threadIdx.x; p < G::BM * G::BN / 4; p += kThreads) {
+      const int m = tm * G::BM + p / (G::BN / 4), n = tn * G::BN + 4 * (p % (G::BN / 4));
+      if (m < N && n < K) *reinterpret_cast<uint2*>(Ce + (int64_t)m * K + n) = make_uint2(0u, 0u);
+    }
+    return;
+  }
+  Tile t;
+  t.A = A + (int64_t)es.base * BK; t.sA = sA + (int64_t)es.base * N; t.sa_stride = N;
+  t.B = B + (int64_t)es.base * BK; t.sB = sB + (int64_t)es.base * K;
+  t.C = Ce; t.Q = nullptr; t.sQ = nullptr;
+  t.m0 = tm * G::BM; t.row_end = N;
+  t.n0 = tn * G::BN; t.N = K; t.K = groups * BK; t.ld = ld;
+  run_tile<G, 1>(t, smem);
 }
 
 // Estimated cost of a tile shape: full rounds of tiles over the CUs times the
@@ -758,6 +776,19 @@ hipError_t launch_grouped_gemm_blockscaled(const uint8_t* A, const float* sA, co
   // out a full HBM latency).
   if (M_total < (int64_t)E * 256) return launch(Cfg128x256d{});
   return launch(Cfg256x256{});
+}
+
+hipError_t launch_grouped_gemm_wgrad(const uint8_t* A, const float* sA, const uint8_t* B,
+                                     const float* sB, uint16_t* C, const int32_t* offsets, int E,
+                                     int64_t M_total, int64_t N, int64_t K, int64_t ld,
+                                     hipStream_t stream) {
+  using namespace gemm;
+  using G = Cfg256x256;
+  const int64_t per_expert = ((N + G::BM - 1) / G::BM) * ((K + G::BN - 1) / G::BN);
+  const int64_t tiles = (int64_t)E * kXcds * ((per_expert + kXcds - 1) / kXcds);
+  hipLaunchKernelGGL((grouped_wgrad_kernel<G>), dim3((unsigned)tiles), dim3(kThreads), 0, stream, A, sA, B,
+                     sB, C, offsets, (int)M_total, (int)N, (int)K, (int)ld);
+  return hipGetLastError();
 }
 
 }  // namespace fp8bs

@@ -19,6 +19,13 @@ hipError_t launch_gemm_blockscaled(const uint8_t* A, const float* sA, const uint
 hipError_t launch_gemm_blockscaled_q1x128(const uint8_t* A, const float* sA, const uint8_t* B,
                                           const float* sB, int row_mode, uint8_t* Q, float* sQ,
                                           int64_t M, int64_t N, int64_t K, hipStream_t stream);
+hipError_t launch_grouped_gemm_wgrad(const uint8_t* A, const float* sA, const uint8_t* B,
+                                     const float* sB, uint16_t* C, const int32_t* offsets, int E,
+                                     int64_t M_total, int64_t N, int64_t K, int64_t ld,
+                                     hipStream_t stream);
+hipError_t launch_quant_act_128x1_T_grouped(const void* x, bool bf16, int64_t M_total, int64_t C,
+                                            const int32_t* offsets, int E, int64_t ld, uint8_t* qT,
+                                            float* sT, hipStream_t stream);
 hipError_t launch_grouped_gemm_blockscaled(const uint8_t* A, const float* sA, const uint8_t* B,
                                            const float* sB, uint16_t* C, const int32_t* offsets,
                                            int E, int64_t M_total, int64_t N, int64_t K,

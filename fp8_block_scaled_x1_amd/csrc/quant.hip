@@ -257,35 +257,58 @@ __global__ __launch_bounds__(256) void quant_act_128x1_T_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// 128x1 transposed quantizer for C % 8 == 0: one workgroup per (token chunk
-// tb, 64 channels), 16-byte loads and an LDS transpose of the codes.
+// 128x1 transposed quantizer for C % 8 == 0: one workgroup per (token group
+// g, 64 channels), 16-byte loads and an LDS transpose of the codes.
 // Lane l of wave w holds channels c0 + 8(l%8) .. +7 of tokens
-// 32w + 4(l/8) .. +3: each load instruction reads 8 whole 128-byte token rows.
-// Per-channel amax: a max over the lane's 4 tokens, then over the 32 token
-// slices through LDS. Each lane encodes its 4 tokens of each of its channels
-// (4 bytes of a qT row) into an LDS tile [channel][token], which is written
-// out as 16-byte pieces, 8 lanes per 128-byte qT row.
+// 32w + 4(l/8) .. +3 of the group: each load instruction reads 8 whole
+// 128-byte token rows. Per-channel amax: a max over the lane's 4 tokens, then
+// over the 32 token slices through LDS. Each lane encodes its 4 tokens of each
+// of its channels (4 bytes of a qT row) into an LDS tile [channel][token],
+// which is written out as 16-byte pieces, 8 lanes per 128-byte qT row.
+//
+// GROUPED: the tokens are per-expert row ranges [off[e], off[e+1]); each
+// expert's tokens are cut into groups of 128 from its first row, its last
+// group padded with zeros (+0 codes) to 128 columns of qT, and the groups of
+// all experts are numbered expert-major: group g = (experts' groups before e)
+// + j covers rows off[e] + 128 j .. and qT columns 128 g .. 128 g + 127, with
+// scales in row g of sT. Otherwise group g is rows 128 g .. 128 g + 127.
+// ld is the row length of qT (M when not grouped).
 // ---------------------------------------------------------------------------
 constexpr int kTPitch = kGroup + 16;   // tile row pitch in bytes (16-byte aligned)
 
-template <bool BF16>
+template <bool BF16, bool GROUPED>
 __global__ __launch_bounds__(256) void quant_act_128x1_T_v8_kernel(
-    const void* __restrict__ x, int64_t M, int C, uint8_t* __restrict__ qT, float* __restrict__ sT) {
+    const void* __restrict__ x, int64_t M, int C, uint8_t* __restrict__ qT, float* __restrict__ sT,
+    const int32_t* __restrict__ off, int E, int64_t ld) {
   __shared__ float red[32][65];
   __shared__ float scl[64];
   __shared__ __align__(16) uint8_t tile[64 * kTPitch];
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int cg = lane & 7, ts = lane >> 3;
-  const int tb = blockIdx.y;
+  const int g = blockIdx.y;
+  int64_t row0 = (int64_t)g * kGroup;   // first input row of the group
+  int n_rows = kGroup;                  // its valid rows
+  if constexpr (GROUPED) {
+    const ExpertSlot es = locate_expert(off, E, (int)M, g, kGroup, 1);
+    if (es.e < 0) return;               // past the last group (uniform over the workgroup)
+    row0 = es.r0 + (int64_t)kGroup * (g - es.base);
+    n_rows = min(kGroup, es.r1 - (int)row0);
+  }
   const int c0 = blockIdx.x * 64;
   const int ch = c0 + 8 * cg;
   const bool cok = ch < C;   // C % 8 == 0: all 8 channels valid or none
-  const int tl = 32 * w + 4 * ts;            // first of this lane's 4 tokens within the chunk
-  const int64_t tok = (int64_t)tb * kGroup + tl;
+  const int tl = 32 * w + 4 * ts;            // first of this lane's 4 tokens within the group
 
   float v[4][8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) load8<BF16>(x, (tok + i) * C + (cok ? ch : 0), v[i]);
+  for (int i = 0; i < 4; ++i) {
+    const int r = GROUPED ? min(tl + i, n_rows - 1) : tl + i;
+    load8<BF16>(x, (row0 + r) * C + (cok ? ch : 0), v[i]);
+    if (GROUPED && tl + i >= n_rows) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[i][j] = 0.0f;
+    }
+  }
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const float m = fmaxf(fmaxf(fabsf(v[0][j]), fabsf(v[1][j])), fmaxf(fabsf(v[2][j]), fabsf(v[3][j])));
@@ -298,14 +321,14 @@ __global__ __launch_bounds__(256) void quant_act_128x1_T_v8_kernel(
     for (int r = 1; r < 32; ++r) amax = fmaxf(amax, red[r][t]);
     const float sc = group_scale(amax);
     scl[t] = sc;
-    if (c0 + t < C) sT[(int64_t)tb * C + c0 + t] = sc;
+    if (c0 + t < C) sT[(int64_t)g * C + c0 + t] = sc;
   }
   __syncthreads();
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const GroupDiv g = group_div_of_scale<BF16>(scl[8 * cg + j]);
+    const GroupDiv gd = group_div_of_scale<BF16>(scl[8 * cg + j]);
     *reinterpret_cast<uint32_t*>(tile + (8 * cg + j) * kTPitch + tl) =
-        e4m3_div_pack4_t<BF16>(v[0][j], v[1][j], v[2][j], v[3][j], g);
+        e4m3_div_pack4_t<BF16>(v[0][j], v[1][j], v[2][j], v[3][j], gd);
   }
   __syncthreads();
 #pragma unroll
@@ -313,7 +336,7 @@ __global__ __launch_bounds__(256) void quant_act_128x1_T_v8_kernel(
     const int p = t + 256 * k;
     const int r = p >> 3, piece = p & 7;
     if (c0 + r < C)
-      *reinterpret_cast<uint4*>(qT + (int64_t)(c0 + r) * M + (int64_t)tb * kGroup + 16 * piece) =
+      *reinterpret_cast<uint4*>(qT + (int64_t)(c0 + r) * ld + (int64_t)g * kGroup + 16 * piece) =
           *reinterpret_cast<const uint4*>(tile + r * kTPitch + 16 * piece);
   }
 }
@@ -354,9 +377,11 @@ hipError_t launch_quant_act_128x1_T(const void* x, bool bf16, int64_t M, int64_t
   const dim3 grid((unsigned)((C + 63) / 64), (unsigned)(M / kGroup));
   if (C % 8 == 0) {
     if (bf16)
-      hipLaunchKernelGGL(quant_act_128x1_T_v8_kernel<true>, grid, dim3(256), 0, stream, x, M, (int)C, qT, sT);
+      hipLaunchKernelGGL((quant_act_128x1_T_v8_kernel<true, false>), grid, dim3(256), 0, stream, x, M, (int)C,
+                         qT, sT, nullptr, 0, M);
     else
-      hipLaunchKernelGGL(quant_act_128x1_T_v8_kernel<false>, grid, dim3(256), 0, stream, x, M, (int)C, qT, sT);
+      hipLaunchKernelGGL((quant_act_128x1_T_v8_kernel<false, false>), grid, dim3(256), 0, stream, x, M, (int)C,
+                         qT, sT, nullptr, 0, M);
     return hipGetLastError();
   }
   const bool pair = (C % 2) == 0;
@@ -368,6 +393,20 @@ hipError_t launch_quant_act_128x1_T(const void* x, bool bf16, int64_t M, int64_t
     hipLaunchKernelGGL((quant_act_128x1_T_kernel<false, true>), grid, dim3(256), 0, stream, x, M, (int)C, qT, sT);
   else
     hipLaunchKernelGGL((quant_act_128x1_T_kernel<false, false>), grid, dim3(256), 0, stream, x, M, (int)C, qT, sT);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_act_128x1_T_grouped(const void* x, bool bf16, int64_t M_total, int64_t C,
+                                            const int32_t* offsets, int E, int64_t ld, uint8_t* qT,
+                                            float* sT, hipStream_t stream) {
+  // ld / 128 bounds the number of groups (validated: ld >= M_total + 127 E)
+  const dim3 grid((unsigned)((C + 63) / 64), (unsigned)(ld / kGroup));
+  if (bf16)
+    hipLaunchKernelGGL((quant_act_128x1_T_v8_kernel<true, true>), grid, dim3(256), 0, stream, x, M_total, (int)C,
+                       qT, sT, offsets, E, ld);
+  else
+    hipLaunchKernelGGL((quant_act_128x1_T_v8_kernel<false, true>), grid, dim3(256), 0, stream, x, M_total, (int)C,
+                       qT, sT, offsets, E, ld);
   return hipGetLastError();
 }
 

@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define FP8BS_ABI_VERSION 2
+#define FP8BS_ABI_VERSION 3
 
 #ifndef FP8BS_API
 #define FP8BS_API __attribute__((visibility("default")))
@@ -164,6 +164,47 @@ FP8BS_API int fp8_grouped_gemm_blockscaled(const uint8_t* A, const float* sA,
                                  uint16_t* C, const int32_t* group_offsets,
                                  int E, int64_t M_total, int64_t N, int64_t K,
                                  void* stream);
+
+/*
+ * Wgrad-operand quantization per expert (128x1 groups as in
+ * fp8_quant_act_128x1_T, report sections 3.3.1-3.3.2 on the innerforce.co.kr
+ * page, applied to the per-expert token batches of the grouped form, report
+ * section 3.4.2 on "Deepseek : The Ultimate Convenience!"). Expert e owns the
+ * rows [off[e], off[e+1]) of x; its tokens are cut into groups of 128 from
+ * its first row, and its last group is padded with zero tokens (+0 codes).
+ * Groups are numbered expert-major: with P_e = sum_{e' < e} ceil(M_e' / 128),
+ * group P_e + j holds rows off[e] + 128 j .. of expert e and lands in the qT
+ * columns 128 (P_e + j) .. 128 (P_e + j) + 127 and in row P_e + j of sT.
+ *   x    [M_total][C]    F32 or BF16 (dtype), rows grouped by expert
+ *   qT   [C][ld]         uint8 codes; columns 128 * P_E .. ld-1 are not written
+ *   sT   [ld/128][C]     float32; rows P_E .. are not written
+ *   group_offsets  DEVICE int32[E+1], off[0] = 0, non-decreasing,
+ *                  off[E] = M_total (precondition as for the grouped GEMM)
+ * C a multiple of 128; ld a multiple of 128 with ld >= M_total + 127 E (room
+ * for every expert's padding); E >= 0, M_total >= 0 (M_total == 0: no-op).
+ * FP8BS_ERR_TOO_LARGE if M_total >= 2^31 or ld / 128 > 65535.
+ */
+FP8BS_API int fp8_quant_act_128x1_T_grouped(const void* x, int dtype, int64_t M_total, int64_t C,
+                          const int32_t* group_offsets, int E, int64_t ld,
+                          uint8_t* qT, float* sT, void* stream);
+
+/*
+ * Per-expert Wgrad GEMM (the FP8 Wgrad GEMM of report sections 3.3.1-3.3.2,
+ * innerforce.co.kr page, in the grouped form of the MoE experts): for every
+ * expert e, with the groups of fp8_quant_act_128x1_T_grouped,
+ *   C[e][n][k] = bf16( sum_{g of e} sA[g][n] * sB[g][k] * sum_{t in g} A[n][t]*B[k][t] )
+ * i.e. dW_e = dY_e^T X_e over expert e's tokens (row-mode scales on both
+ * operands, per-group FP32 promotion as in fp8_gemm_blockscaled).
+ *   A  [N][ld]  uint8, sA [ld/128][N]  fp8_quant_act_128x1_T_grouped of dY[M_total][N]
+ *   B  [K][ld]  uint8, sB [ld/128][K]  fp8_quant_act_128x1_T_grouped of X[M_total][K]
+ *   C  [E][N][K]  BF16 bits; an expert without tokens gets zeros
+ *   group_offsets, E, M_total, ld  exactly as given to both quantizer calls
+ * N and K multiples of 128; N*ld and K*ld below 2^31.
+ */
+FP8BS_API int fp8_grouped_gemm_wgrad(const uint8_t* A, const float* sA, const uint8_t* B,
+                          const float* sB, uint16_t* C, const int32_t* group_offsets,
+                          int E, int64_t M_total, int64_t N, int64_t K, int64_t ld,
+                          void* stream);
 
 /* Human-readable name of a status code (static string). */
 FP8BS_API const char* fp8bs_status_string(int status);

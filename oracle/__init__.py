@@ -18,7 +18,9 @@ Sources (the DeepSeek-V3 technical report as paraphrased on the pages):
     and accumulated there in full FP32 precision.
   * the page headed "Deepseek : The Ultimate Convenience!", report sections
     3.3.2 and 3.5.2: per-group scaling along the inner dimension again, and the
-    remark that fusing a transposition into the GEMM is cumbersome.
+    remark that fusing a transposition into the GEMM is cumbersome; report
+    section 3.4.2: every MoE expert works on its own batch of tokens (the
+    grouped forms).
 
 Where the pages leave a step open (group geometry 1x128 / 128x128 / 128x1,
 the OCP E4M3FN variant with max 448, scale = amax/448 in FP32, RNE, the
@@ -34,11 +36,13 @@ from .e4m3 import (E4M3_MAX, e4m3_decode, e4m3_encode, e4m3_finite_values)
 from .quant import (GROUP, bf16_bits_to_f32, group_scale, quant_act_1x128,
                     quant_act_128x1_T, quant_w_128x128)
 from .gemm import gemm_ref, grouped_gemm_ref, gemm_ref_rows
+from .grouped import grouped_wgrad_ref, padded_group_starts, quant_act_128x1_T_grouped
 from .tolerance import bf16_ulp, check_gemm, bf16_bits_to_f64
 
 __all__ = [
     "E4M3_MAX", "e4m3_decode", "e4m3_encode", "e4m3_finite_values", "GROUP",
     "bf16_bits_to_f32", "group_scale", "quant_act_1x128", "quant_act_128x1_T",
     "quant_w_128x128", "gemm_ref", "grouped_gemm_ref", "gemm_ref_rows",
-    "bf16_ulp", "check_gemm", "bf16_bits_to_f64",
+    "bf16_ulp", "check_gemm", "bf16_bits_to_f64", "grouped_wgrad_ref", "padded_group_starts",
+    "quant_act_128x1_T_grouped",
 ]

@@ -21,6 +21,10 @@ BF16, cast to bfloat16 by torch (round to nearest even).
                   W_up[32][4096][7168], W_dn[32][7168][2048] bf16 N(0,0.01)
   decode_grouped  32 experts, M_e uniform in 1..256 (numpy rng(seed));
                   A[sum][7168] bf16 N(0,1); W[32][4096][7168] bf16 N(0,0.01)
+  grouped_moe_backward
+                  grouped_moe's routing, activations and weights (same seed),
+                  then dY_up[sum][4096] and dY_dn[sum][7168] bf16 N(0,1e-3),
+                  each with 1% of its rows (random) x100
   backward_pair   dY[4096][7168] bf16 N(0,1e-3) with 1% (41) random rows x100;
                   X[4096][7168] bf16 N(0,1) with 4 random columns x100;
                   W as dense_fprop's weight (same draw with the same seed)
@@ -96,6 +100,20 @@ def grouped_moe(device="cpu", seed=0, tokens=8192, experts=32, topk=8, alpha=0.5
     return out
 
 
+def grouped_moe_backward(device="cpu", seed=0, tokens=8192, experts=32, topk=8, alpha=0.5,
+                         d_model=7168, d_ff2=4096, d_ff=2048, outlier_row_frac=0.01):
+    """grouped_moe's inputs plus the output gradients of the up and down GEMMs."""
+    out = grouped_moe(device, seed, tokens, experts, topk, alpha, d_model, d_ff2, d_ff)
+    total = int(out["offsets"][-1])
+    g = _gen(device, seed + 2)
+    for key, width in (("dY_up", d_ff2), ("dY_dn", d_model)):
+        dY = _randn((total, width), 1e-3, g, device)
+        rows = _pick(total, int(round(outlier_row_frac * total)), g, device)
+        dY[rows, :] *= 100.0
+        out[key] = dY.to(torch.bfloat16)
+    return out
+
+
 def decode_counts(seed=0, experts=32, max_tokens=256):
     rng = np.random.default_rng(seed)
     counts = rng.integers(1, max_tokens + 1, experts).astype(np.int64)
@@ -137,5 +155,5 @@ def ceil_div(a, b):
     return -(-a // b)
 
 
-__all__ = ["tiny_fprop", "dense_fprop", "moe_routing", "grouped_moe", "decode_counts",
+__all__ = ["tiny_fprop", "dense_fprop", "moe_routing", "grouped_moe", "grouped_moe_backward", "decode_counts",
            "decode_grouped", "backward_pair", "gemm_flops", "ceil_div"]
