@@ -8,8 +8,9 @@ promotion per 128-wide K chunk, BF16 output). Other workloads (--workload)
 measure the remaining forms of the path: the backward pair (Dgrad + Wgrad with
 the 128x1 transposed quantizer), the grouped MoE expert GEMMs and their
 backward (grouped Dgrad, grouped 128x1 transposed quantizers, per-expert
-Wgrad), the decode-shaped grouped GEMM, and the Fprop whose GEMM writes the
-next layer's 1x128-quantized input directly (fused quantizing epilogue).
+Wgrad), the MoE dispatch with its FP8 payload and the BF16 combine, the
+decode-shaped grouped GEMM, and the Fprop whose GEMM writes the next layer's
+1x128-quantized input directly (fused quantizing epilogue).
 
 Prints one JSON line. `value` is whole-step throughput with inputs resident in
 HBM; `roofline` describes the dominant kernel, timed live with HIP events on
@@ -371,6 +372,52 @@ def setup_moe_backward(torch, fb, dev):
     return step, info
 
 
+def setup_moe_dispatch(torch, fb, dev):
+    """MoE dispatch with the FP8 payload (routing, permute + 1x128 quantize into
+    the grouped GEMM's layout) and the BF16 combine of the experts' outputs."""
+    import workloads
+    d = workloads.moe_dispatch(device=dev)
+    T, K = d["X"].shape
+    topk, E = d["ids"].shape[1], 32
+    P = T * topk
+    ids = torch.from_numpy(d["ids"]).to(dev)
+    w = torch.from_numpy(d["w"]).to(dev)
+    X, Y = d["X"], d["Y"]
+    L = fb.lib()
+    ws = torch.empty(max(L.fp8_moe_dispatch_workspace_bytes(T, topk, E) // 4, 1), dtype=torch.int32, device=dev)
+    q = torch.empty((P, K), dtype=torch.uint8, device=dev)
+    s = torch.empty((K // 128, P), dtype=torch.float32, device=dev)
+    off = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    pos = torch.empty((T, topk), dtype=torch.int32, device=dev)
+    src = torch.empty(P, dtype=torch.int32, device=dev)
+    out = torch.empty((T, K), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+
+    def step(timer):
+        timer.mark()
+        rc = L.fp8_moe_dispatch(X.data_ptr(), fb.BF16, T, K, ids.data_ptr(), topk, E, q.data_ptr(), s.data_ptr(),
+                                off.data_ptr(), pos.data_ptr(), src.data_ptr(), ws.data_ptr(), stream)
+        timer.mark()
+        rc |= L.fp8_moe_combine(Y.data_ptr(), pos.data_ptr(), w.data_ptr(), T, topk, K, out.data_ptr(), stream)
+        timer.mark()
+        if rc:
+            raise RuntimeError(f"libfp8bs call failed ({rc})")
+
+    disp = T * K * 2 + P * K + P * (K // 128) * 4 + P * 4 * 3     # x in; codes, scales, ids/pos/src
+    comb = P * K * 2 + T * K * 2 + P * 8                           # Y in, out, pos + weights
+    info = {
+        "names": ["moe_dispatch", "moe_combine"],
+        "step_flops": 0.0,
+        "step_bytes": disp + comb,
+        "work": {"moe_dispatch": ("GB/s", disp), "moe_combine": ("GB/s", comb)},
+        "dominant": "moe_combine",
+        "config": {"workload": f"MoE dispatch + combine: {T} tokens x top-{topk} of {E} experts "
+                               f"(Dirichlet(0.5)), d_model {K}; payload FP8 1x128, combine BF16",
+                   "tokens": T, "topk": topk, "E": E, "K": K},
+    }
+    return step, info
+
+
 def setup_decode(torch, fb, dev):
     """Decode-shaped grouped GEMM: 32 experts, 1..256 rows each, weights pre-quantized."""
     import workloads
@@ -429,7 +476,7 @@ def setup_copy(torch, fb, dev, nbytes=None):
 
 WORKLOADS = {"copy": setup_copy, "dense_fprop": setup_dense_fprop, "fprop_q1x128": setup_fprop_q1x128,
              "backward": setup_backward, "moe": setup_moe, "moe_backward": setup_moe_backward,
-             "decode": setup_decode}
+             "moe_dispatch": setup_moe_dispatch, "decode": setup_decode}
 
 
 # ---------------------------------------------------------------------------
@@ -462,6 +509,22 @@ def cpu_baseline(workload):
         nbytes = N * K + M * K + M * N * 2
         return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
                 "sample": f"one decode expert: GEMM {M}x{N}x{K} (pre-quantized operands), {dt:.1f} s"}
+    if workload == "moe_dispatch":
+        # 1024 tokens x top-8 of 32 experts, d_model 7168: route, quantize, permute; combine
+        import workloads
+        T, K, topk = 1024, 7168, 8
+        ids, wts = workloads.moe_topk(0, T, 32, topk)
+        X = torch.randn(T, K, generator=g).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        Y = torch.randn(T * topk, K, generator=g).to(torch.bfloat16).float().numpy()
+        t0 = time.perf_counter()
+        _, _, _, pos, _ = oracle.dispatch_quant(X, ids, 32)
+        oracle.combine_ref(Y, pos, wts)
+        dt = time.perf_counter() - t0
+        P = T * topk
+        nbytes = T * K * 2 + P * K + P * (K // 128) * 4 + P * 12 + P * K * 2 + T * K * 2 + P * 8
+        return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
+                "sample": f"{T} tokens x top-{topk}, K={K}: dispatch (route, quantize, permute) and combine; "
+                          f"{dt:.1f} s"}
     if workload == "moe_backward":
         # one expert's Wgrad: 1000 tokens (8 groups, the last one padded), dW 4096 x 7168
         T, N, K = 1000, 4096, 7168

@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libfp8bs.so")
 
 F32, BF16 = 0, 1
 SCALE_BLOCK128, SCALE_ROW = 0, 1
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 _c_int64 = ctypes.c_int64
 _vp = ctypes.c_void_p
@@ -35,6 +35,10 @@ _SIGNATURES = {
                                       _vp, _vp],
     "fp8_grouped_gemm_wgrad": [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _c_int64, _c_int64, _c_int64,
                                _c_int64, _vp],
+    "fp8_moe_dispatch": [_vp, ctypes.c_int, _c_int64, _c_int64, _vp, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp,
+                         _vp, _vp, _vp, _vp],
+    "fp8_moe_dispatch_workspace_bytes": [_c_int64, ctypes.c_int, ctypes.c_int],
+    "fp8_moe_combine": [_vp, _vp, _vp, _c_int64, ctypes.c_int, _c_int64, _vp, _vp],
     "fp8bs_status_string": [ctypes.c_int],
     "fp8bs_abi_version": [],
 }
@@ -58,7 +62,8 @@ def lib():
         for name, args in _SIGNATURES.items():
             fn = getattr(handle, name)
             fn.argtypes = args
-            fn.restype = ctypes.c_char_p if name == "fp8bs_status_string" else ctypes.c_int
+            fn.restype = {"fp8bs_status_string": ctypes.c_char_p,
+                          "fp8_moe_dispatch_workspace_bytes": ctypes.c_int64}.get(name, ctypes.c_int)
         if handle.fp8bs_abi_version() != ABI_VERSION:
             raise ImportError(f"libfp8bs ABI {handle.fp8bs_abi_version()} != {ABI_VERSION}")
         _lib = handle
@@ -257,4 +262,47 @@ def fp8_grouped_gemm_wgrad(A, sA, B, sB, group_offsets, M_total, out=None):
         raise ValueError("out has the wrong shape")
     _check("fp8_grouped_gemm_wgrad",
            lib().fp8_grouped_gemm_wgrad(pa, psa, pb, psb, pc, po, E, int(M_total), N, K, ld, _stream(A)))
+    return out
+
+
+def fp8_moe_dispatch(x, topk_ids, E):
+    """Route token copies to experts and quantize the payload 1x128.
+
+    x[T][K] f32|bf16, topk_ids[T][topk] int32 (GPU) -> (q uint8 [T*topk][K],
+    s float32 [K/128][T*topk], offsets int32 [E+1], pos int32 [T][topk],
+    src_row int32 [T*topk]); rows sorted by expert, then token, then slot.
+    """
+    if x.dim() != 2 or topk_ids.dim() != 2 or topk_ids.shape[0] != x.shape[0]:
+        raise ValueError("x must be [T][K] and topk_ids [T][topk]")
+    T, K = x.shape
+    topk = topk_ids.shape[1]
+    px = _dev(x, "x", (torch.float32, torch.bfloat16))
+    pid = _dev(topk_ids, "topk_ids", (torch.int32,))
+    L = lib()
+    ws_bytes = L.fp8_moe_dispatch_workspace_bytes(T, topk, E)
+    _check("fp8_moe_dispatch_workspace_bytes", min(0, ws_bytes))
+    dev = x.device
+    ws = torch.empty(max(ws_bytes // 4, 1), dtype=torch.int32, device=dev)
+    q = torch.empty((T * topk, K), dtype=torch.uint8, device=dev)
+    s = torch.empty((K // 128 if K % 128 == 0 else 0, T * topk), dtype=torch.float32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    pos = torch.empty((T, topk), dtype=torch.int32, device=dev)
+    src = torch.empty(T * topk, dtype=torch.int32, device=dev)
+    _check("fp8_moe_dispatch",
+           L.fp8_moe_dispatch(px, _in_dtype(x), T, K, pid, topk, E, q.data_ptr(), s.data_ptr(), offsets.data_ptr(),
+                              pos.data_ptr(), src.data_ptr(), ws.data_ptr(), _stream(x)))
+    return q, s, offsets, pos, src
+
+
+def fp8_moe_combine(Y, pos, w):
+    """out[T][N] bf16 = sum over slots j of w[t][j] * Y[pos[t][j]] (FP32 sums in slot order)."""
+    T, topk = pos.shape
+    N = Y.shape[1]
+    if tuple(w.shape) != (T, topk) or Y.shape[0] != T * topk:
+        raise ValueError("Y, pos and w disagree")
+    py = _dev(Y, "Y", (torch.bfloat16,))
+    pp = _dev(pos, "pos", (torch.int32,))
+    pw = _dev(w, "w", (torch.float32,))
+    out = torch.empty((T, N), dtype=torch.bfloat16, device=Y.device)
+    _check("fp8_moe_combine", lib().fp8_moe_combine(py, pp, pw, T, topk, N, out.data_ptr(), _stream(Y)))
     return out

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfp8bs.so")
-SOURCES = ["api.hip", "quant.hip", "gemm.hip"]
+SOURCES = ["api.hip", "quant.hip", "gemm.hip", "moe.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

@@ -156,4 +156,41 @@ int fp8_grouped_gemm_wgrad(const uint8_t* A, const float* sA, const uint8_t* B, 
                                                     as_stream(stream)));
 }
 
+int64_t fp8_moe_dispatch_workspace_bytes(int64_t T, int topk, int E) {
+  if (T < 0 || topk < 1 || topk > 64 || E < 1 || E > fp8bs::moe_max_experts()) return FP8BS_ERR_SHAPE;
+  if (T * topk >= kI32) return FP8BS_ERR_TOO_LARGE;
+  return 4 * (int64_t)E * fp8bs::moe_route_blocks(T * topk);
+}
+
+int fp8_moe_dispatch(const void* x, int dtype, int64_t T, int64_t K, const int32_t* topk_ids, int topk, int E,
+                     uint8_t* q, float* s, int32_t* offsets, int32_t* pos, int32_t* src_row, void* workspace,
+                     void* stream) {
+  if (!valid_dtype(dtype)) return FP8BS_ERR_DTYPE;
+  if (T < 0 || K < 0 || K % kG || topk < 1 || topk > 64 || E < 1 || E > fp8bs::moe_max_experts())
+    return FP8BS_ERR_SHAPE;
+  const int64_t P = T * topk;
+  if (P >= kI32 || K >= kI32 || (K / kG + 3) / 4 > 65535 || (T + 7) / 8 >= (int64_t)1 << 27)
+    return FP8BS_ERR_TOO_LARGE;
+  if (!offsets) return FP8BS_ERR_NULL_PTR;
+  if (P > 0 && (!topk_ids || !pos || !src_row || !workspace)) return FP8BS_ERR_NULL_PTR;
+  if (P > 0 && K > 0 && (!x || !q || !s)) return FP8BS_ERR_NULL_PTR;
+  if (misaligned(x) || misaligned(q) || misaligned(s)) return FP8BS_ERR_ALIGN;
+  auto mis4 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) != 0; };
+  if (mis4(topk_ids) || mis4(offsets) || mis4(pos) || mis4(src_row) || mis4(workspace)) return FP8BS_ERR_ALIGN;
+  return status_of(fp8bs::launch_moe_dispatch(x, dtype == FP8BS_BF16, T, K, topk_ids, topk, E, q, s, offsets,
+                                              pos, src_row, static_cast<int32_t*>(workspace),
+                                              as_stream(stream)));
+}
+
+int fp8_moe_combine(const uint16_t* Y, const int32_t* pos, const float* w, int64_t T, int topk, int64_t N,
+                    uint16_t* out, void* stream) {
+  if (T < 0 || N < 0 || N % 8 || topk < 1 || topk > 64) return FP8BS_ERR_SHAPE;
+  if (T * topk >= kI32 || N >= kI32 || T * (N / 8) >= kI32 * 64) return FP8BS_ERR_TOO_LARGE;
+  if (T == 0 || N == 0) return FP8BS_OK;
+  if (!Y || !pos || !w || !out) return FP8BS_ERR_NULL_PTR;
+  if (misaligned(Y) || misaligned(out)) return FP8BS_ERR_ALIGN;
+  if ((reinterpret_cast<uintptr_t>(pos) & 3u) || (reinterpret_cast<uintptr_t>(w) & 3u)) return FP8BS_ERR_ALIGN;
+  return status_of(fp8bs::launch_moe_combine(Y, pos, w, T, topk, N, out, as_stream(stream)));
+}
+
 }  // extern "C"

@@ -31,4 +31,12 @@ hipError_t launch_grouped_gemm_blockscaled(const uint8_t* A, const float* sA, co
                                            int E, int64_t M_total, int64_t N, int64_t K,
                                            hipStream_t stream);
 
+int64_t moe_route_blocks(int64_t pairs);
+int moe_max_experts();
+hipError_t launch_moe_dispatch(const void* x, bool bf16, int64_t T, int64_t K, const int32_t* ids, int topk,
+                               int E, uint8_t* q, float* s, int32_t* offsets, int32_t* pos, int32_t* src,
+                               int32_t* ws, hipStream_t stream);
+hipError_t launch_moe_combine(const uint16_t* Y, const int32_t* pos, const float* w, int64_t T, int topk,
+                              int64_t N, uint16_t* out, hipStream_t stream);
+
 }  // namespace fp8bs

@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define FP8BS_ABI_VERSION 3
+#define FP8BS_ABI_VERSION 4
 
 #ifndef FP8BS_API
 #define FP8BS_API __attribute__((visibility("default")))
@@ -205,6 +205,52 @@ FP8BS_API int fp8_grouped_gemm_wgrad(const uint8_t* A, const float* sA, const ui
                           const float* sB, uint16_t* C, const int32_t* group_offsets,
                           int E, int64_t M_total, int64_t N, int64_t K, int64_t ld,
                           void* stream);
+
+/*
+ * MoE dispatch with the payload in FP8 (report section 3.3.3: activations are
+ * quantized to FP8 before they are dispatched to the experts, innerforce.co.kr
+ * page). Routes every (token t, slot j) pair to expert topk_ids[t][j], sorts
+ * the pairs by expert (stable: by t, then j, inside an expert) and writes, in
+ * that row order, the 1x128 quantization of each pair's token row: exactly
+ * the codes and scales fp8_quant_act_1x128 gives for x[t], ready for
+ * fp8_grouped_gemm_blockscaled (A = q, sA = s, group_offsets = offsets,
+ * M_total = T*topk). Each token row is read once.
+ *   x         [T][K]        F32 or BF16 (dtype)
+ *   topk_ids  [T][topk]     int32, DEVICE; experts in [0, E) (precondition;
+ *                           others are treated as the nearest valid id)
+ *   q         [T*topk][K]   uint8 codes, row r = copy of token src_row[r]
+ *   s         [K/128][T*topk] float32
+ *   offsets   [E+1]         int32, expert e owns rows [offsets[e], offsets[e+1])
+ *   pos       [T][topk]     int32, the row of each pair
+ *   src_row   [T*topk]      int32, the token of each row
+ *   workspace DEVICE, at least fp8_moe_dispatch_workspace_bytes(T, topk, E)
+ *             bytes; its contents on entry do not matter
+ * 1 <= E <= 1024, 1 <= topk <= 64, K a multiple of 128, T >= 0 (T == 0 writes
+ * offsets = 0 only). x, q and s 16-byte aligned; the int32 buffers 4-byte.
+ */
+FP8BS_API int fp8_moe_dispatch(const void* x, int dtype, int64_t T, int64_t K,
+                          const int32_t* topk_ids, int topk, int E,
+                          uint8_t* q, float* s, int32_t* offsets, int32_t* pos,
+                          int32_t* src_row, void* workspace, void* stream);
+
+/* Workspace bytes fp8_moe_dispatch needs (negative: invalid sizes). */
+FP8BS_API int64_t fp8_moe_dispatch_workspace_bytes(int64_t T, int topk, int E);
+
+/*
+ * MoE combine in BF16 (report section 3.3.3: the combine is kept in BF16,
+ * why-be.why-be.co.kr page): every token's expert outputs are weighted and
+ * summed back,
+ *   out[t][n] = bf16( sum_{j < topk} w[t][j] * Y[pos[t][j]][n] )
+ * with FP32 fused multiply-adds in slot order j = 0, 1, ... from zero, then
+ * round to nearest even.
+ *   Y    [T*topk][N]  BF16 bits (rows in the order fp8_moe_dispatch gave)
+ *   pos  [T][topk]    int32 from fp8_moe_dispatch
+ *   w    [T][topk]    float32 routing weights
+ *   out  [T][N]       BF16 bits
+ * N a multiple of 8; 1 <= topk <= 64; T >= 0.
+ */
+FP8BS_API int fp8_moe_combine(const uint16_t* Y, const int32_t* pos, const float* w,
+                          int64_t T, int topk, int64_t N, uint16_t* out, void* stream);
 
 /* Human-readable name of a status code (static string). */
 FP8BS_API const char* fp8bs_status_string(int status);

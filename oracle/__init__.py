@@ -37,6 +37,7 @@ from .quant import (GROUP, bf16_bits_to_f32, group_scale, quant_act_1x128,
                     quant_act_128x1_T, quant_w_128x128)
 from .gemm import gemm_ref, grouped_gemm_ref, gemm_ref_rows
 from .grouped import grouped_wgrad_ref, padded_group_starts, quant_act_128x1_T_grouped
+from .dispatch import check_combine, combine_ref, dispatch_quant, route
 from .tolerance import bf16_ulp, check_gemm, bf16_bits_to_f64
 
 __all__ = [
@@ -44,5 +45,5 @@ __all__ = [
     "bf16_bits_to_f32", "group_scale", "quant_act_1x128", "quant_act_128x1_T",
     "quant_w_128x128", "gemm_ref", "grouped_gemm_ref", "gemm_ref_rows",
     "bf16_ulp", "check_gemm", "bf16_bits_to_f64", "grouped_wgrad_ref", "padded_group_starts",
-    "quant_act_128x1_T_grouped",
+    "quant_act_128x1_T_grouped", "check_combine", "combine_ref", "dispatch_quant", "route",
 ]

@@ -14,9 +14,13 @@ BF16, cast to bfloat16 by torch (round to nearest even).
                   W[512][1024] f32 N(0,0.02)
   dense_fprop     X[4096][7168] bf16 N(0,1), 1% (72) random columns x50;
                   W[7168][7168] bf16 N(0,0.006)
-  moe_routing     8192 tokens, p ~ Dirichlet(0.5 * 1_32), each token picks 8
-                  distinct experts without replacement with probabilities p;
-                  rows are grouped by expert -> per-expert counts and offsets
+  moe_topk        8192 tokens, p ~ Dirichlet(0.5 * 1_32), each token picks 8
+                  distinct experts without replacement with probabilities p
+                  (numpy rng(seed)); weights = p of the picks, renormalised
+  moe_routing     moe_topk's picks grouped by expert -> per-expert counts and
+                  offsets
+  moe_dispatch    moe_topk's picks and weights; X[8192][7168] bf16 N(0,1);
+                  Y[65536][7168] bf16 N(0,1) (the experts' outputs)
   grouped_moe     A_up[sum][7168], A_dn[sum][2048] bf16 N(0,1);
                   W_up[32][4096][7168], W_dn[32][7168][2048] bf16 N(0,0.01)
   decode_grouped  32 experts, M_e uniform in 1..256 (numpy rng(seed));
@@ -74,16 +78,35 @@ def dense_fprop(device="cpu", seed=0, M=4096, N=7168, K=7168, outlier_frac=0.01,
     return {"X": X, "W": W}
 
 
-def moe_routing(seed=0, tokens=8192, experts=32, topk=8, alpha=0.5):
-    """Per-expert row counts and int32 offsets[E+1] of the expert-sorted rows."""
+def moe_topk(seed=0, tokens=8192, experts=32, topk=8, alpha=0.5):
+    """Expert ids [tokens][topk] (int32) and routing weights [tokens][topk]
+    (float32, the draw's probabilities renormalised over each token's experts)."""
     rng = np.random.default_rng(seed)
     p = rng.dirichlet(np.full(experts, alpha))
-    counts = np.zeros(experts, np.int64)
-    for _ in range(tokens):
-        counts[rng.choice(experts, topk, replace=False, p=p)] += 1
+    ids = np.empty((tokens, topk), np.int32)
+    for t in range(tokens):
+        ids[t] = rng.choice(experts, topk, replace=False, p=p)
+    w = p[ids]
+    w = (w / w.sum(axis=1, keepdims=True)).astype(np.float32)
+    return ids, w
+
+
+def moe_routing(seed=0, tokens=8192, experts=32, topk=8, alpha=0.5):
+    """Per-expert row counts and int32 offsets[E+1] of the expert-sorted rows."""
+    ids, _ = moe_topk(seed, tokens, experts, topk, alpha)
+    counts = np.bincount(ids.reshape(-1), minlength=experts).astype(np.int64)
     offsets = np.zeros(experts + 1, np.int32)
     offsets[1:] = np.cumsum(counts)
     return counts, offsets
+
+
+def moe_dispatch(device="cpu", seed=0, tokens=8192, experts=32, topk=8, alpha=0.5, d_model=7168):
+    """Token activations, their routing and the experts' outputs to combine."""
+    ids, w = moe_topk(seed, tokens, experts, topk, alpha)
+    g = _gen(device, seed + 3)
+    X = _randn((tokens, d_model), 1.0, g, device, torch.bfloat16)
+    Y = _randn((tokens * topk, d_model), 1.0, g, device, torch.bfloat16)
+    return {"ids": ids, "w": w, "X": X, "Y": Y}
 
 
 def grouped_moe(device="cpu", seed=0, tokens=8192, experts=32, topk=8, alpha=0.5,
@@ -155,5 +178,5 @@ def ceil_div(a, b):
     return -(-a // b)
 
 
-__all__ = ["tiny_fprop", "dense_fprop", "moe_routing", "grouped_moe", "grouped_moe_backward", "decode_counts",
+__all__ = ["tiny_fprop", "dense_fprop", "moe_topk", "moe_routing", "moe_dispatch", "grouped_moe", "grouped_moe_backward", "decode_counts",
            "decode_grouped", "backward_pair", "gemm_flops", "ceil_div"]
