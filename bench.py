@@ -9,8 +9,9 @@ measure the remaining forms of the path: the backward pair (Dgrad + Wgrad with
 the 128x1 transposed quantizer), the grouped MoE expert GEMMs and their
 backward (grouped Dgrad, grouped 128x1 transposed quantizers, per-expert
 Wgrad), the MoE dispatch with its FP8 payload and the BF16 combine, the
-decode-shaped grouped GEMM, and the Fprop whose GEMM writes the next layer's
-1x128-quantized input directly (fused quantizing epilogue).
+decode-shaped grouped GEMM, the Fprop whose GEMM writes the next layer's
+1x128-quantized input directly (fused quantizing epilogue), and the Fprop with
+power-of-two scales applied by the MFMA itself (E8M0 variant).
 
 Prints one JSON line. `value` is whole-step throughput with inputs resident in
 HBM; `roofline` describes the dominant kernel, timed live with HIP events on
@@ -93,10 +94,11 @@ def _rotations(bytes_per_set, target=600e6):
     return max(2, int(-(-target // bytes_per_set)))
 
 
-def setup_dense_fprop(torch, fb, dev, M=4096, N=7168, K=7168, fused=False):
+def setup_dense_fprop(torch, fb, dev, M=4096, N=7168, K=7168, fused=False, pow2=False):
     """Quantize X 1x128 and W 128x128, then the GEMM. With fused=True the GEMM
     writes the 1x128 quantization of its result (the next layer's FP8 input)
-    instead of the BF16 result."""
+    instead of the BF16 result. With pow2=True the scales are powers of two
+    and the MFMA applies them (E8M0 operand scales)."""
     import workloads
     sets = []
     R = _rotations(M * K * 2 + N * K * 2 + M * K + N * K + M * N * (1 if fused else 2))
@@ -115,6 +117,8 @@ def setup_dense_fprop(torch, fb, dev, M=4096, N=7168, K=7168, fused=False):
         else:
             sets[-1]["C"] = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     L = fb.lib()
+    qa = L.fp8_quant_act_1x128_pow2 if pow2 else L.fp8_quant_act_1x128
+    qw = L.fp8_quant_w_128x128_pow2 if pow2 else L.fp8_quant_w_128x128
     stream = torch.cuda.current_stream(dev).cuda_stream
     state = {"i": 0}
 
@@ -122,12 +126,15 @@ def setup_dense_fprop(torch, fb, dev, M=4096, N=7168, K=7168, fused=False):
         s = sets[state["i"] % R]
         state["i"] += 1
         timer.mark()
-        rc = L.fp8_quant_act_1x128(s["X"].data_ptr(), fb.BF16, M, K, s["qx"].data_ptr(), s["sx"].data_ptr(), stream)
+        rc = qa(s["X"].data_ptr(), fb.BF16, M, K, s["qx"].data_ptr(), s["sx"].data_ptr(), stream)
         timer.mark()
-        rc |= L.fp8_quant_w_128x128(s["W"].data_ptr(), fb.BF16, N, K, s["qw"].data_ptr(), s["sw"].data_ptr(),
-                                    None, None, stream)
+        rc |= qw(s["W"].data_ptr(), fb.BF16, N, K, s["qw"].data_ptr(), s["sw"].data_ptr(), None, None, stream)
         timer.mark()
-        if fused:
+        if pow2:
+            rc |= L.fp8_gemm_blockscaled_pow2(s["qx"].data_ptr(), s["sx"].data_ptr(), s["qw"].data_ptr(),
+                                              s["sw"].data_ptr(), fb.SCALE_BLOCK128, s["C"].data_ptr(), M, N, K,
+                                              stream)
+        elif fused:
             rc |= L.fp8_gemm_blockscaled_q1x128(s["qx"].data_ptr(), s["sx"].data_ptr(), s["qw"].data_ptr(),
                                                 s["sw"].data_ptr(), fb.SCALE_BLOCK128, s["Q"].data_ptr(),
                                                 s["sQ"].data_ptr(), M, N, K, stream)
@@ -139,9 +146,9 @@ def setup_dense_fprop(torch, fb, dev, M=4096, N=7168, K=7168, fused=False):
             raise RuntimeError(f"libfp8bs call failed ({rc})")
 
     flops = 2.0 * M * N * K
-    gemm = "gemm_blockscaled_q1x128" if fused else "gemm_blockscaled"
+    gemm = "gemm_blockscaled_q1x128" if fused else ("gemm_blockscaled_pow2" if pow2 else "gemm_blockscaled")
     out = (f"Q[{M}x{N}] fp8 + sQ[{N // 128}x{M}] (fused 1x128 quantizing epilogue)" if fused
-           else f"C[{M}x{N}] bf16")
+           else f"C[{M}x{N}] bf16" + (", power-of-two scales applied by the MFMA (E8M0)" if pow2 else ""))
     info = {
         "names": ["quant_act_1x128", "quant_w_128x128", gemm],
         "step_flops": flops,
@@ -159,6 +166,10 @@ def setup_dense_fprop(torch, fb, dev, M=4096, N=7168, K=7168, fused=False):
 
 def setup_fprop_q1x128(torch, fb, dev):
     return setup_dense_fprop(torch, fb, dev, fused=True)
+
+
+def setup_fprop_pow2(torch, fb, dev):
+    return setup_dense_fprop(torch, fb, dev, pow2=True)
 
 
 def setup_backward(torch, fb, dev, M=4096, N=7168, K=7168):
@@ -475,6 +486,7 @@ def setup_copy(torch, fb, dev, nbytes=None):
 
 
 WORKLOADS = {"copy": setup_copy, "dense_fprop": setup_dense_fprop, "fprop_q1x128": setup_fprop_q1x128,
+             "fprop_pow2": setup_fprop_pow2,
              "backward": setup_backward, "moe": setup_moe, "moe_backward": setup_moe_backward,
              "moe_dispatch": setup_moe_dispatch, "decode": setup_decode}
 
@@ -543,9 +555,10 @@ def cpu_baseline(workload):
     X = torch.randn(M, K, generator=g).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     W = (torch.randn(N, K, generator=g) * 0.006).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     fused = workload == "fprop_q1x128"
+    pow2 = workload == "fprop_pow2"
     t0 = time.perf_counter()
-    qx, sx = oracle.quant_act_1x128(X)
-    qw, sw = oracle.quant_w_128x128(W)
+    qx, sx = oracle.quant_act_1x128(X, pow2=pow2)
+    qw, sw = oracle.quant_w_128x128(W, pow2=pow2)
     C, _ = oracle.gemm_ref(qx, sx, qw, sw)
     if fused:
         oracle.quant_act_1x128(C.astype(np.float32))

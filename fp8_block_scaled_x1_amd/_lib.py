@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libfp8bs.so")
 
 F32, BF16 = 0, 1
 SCALE_BLOCK128, SCALE_ROW = 0, 1
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 _c_int64 = ctypes.c_int64
 _vp = ctypes.c_void_p
@@ -27,6 +27,10 @@ _SIGNATURES = {
     "fp8_quant_w_128x128": [_vp, ctypes.c_int, _c_int64, _c_int64, _vp, _vp, _vp, _vp, _vp],
     "fp8_quant_act_128x1_T": [_vp, ctypes.c_int, _c_int64, _c_int64, _vp, _vp, _vp],
     "fp8_gemm_blockscaled": [_vp, _vp, _vp, _vp, ctypes.c_int, _vp, _c_int64, _c_int64, _c_int64, _vp],
+    "fp8_quant_act_1x128_pow2": [_vp, ctypes.c_int, _c_int64, _c_int64, _vp, _vp, _vp],
+    "fp8_quant_w_128x128_pow2": [_vp, ctypes.c_int, _c_int64, _c_int64, _vp, _vp, _vp, _vp, _vp],
+    "fp8_quant_act_128x1_T_pow2": [_vp, ctypes.c_int, _c_int64, _c_int64, _vp, _vp, _vp],
+    "fp8_gemm_blockscaled_pow2": [_vp, _vp, _vp, _vp, ctypes.c_int, _vp, _c_int64, _c_int64, _c_int64, _vp],
     "fp8_gemm_blockscaled_q1x128": [_vp, _vp, _vp, _vp, ctypes.c_int, _vp, _vp, _c_int64, _c_int64,
                                     _c_int64, _vp],
     "fp8_grouped_gemm_blockscaled": [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _c_int64, _c_int64,
@@ -99,20 +103,22 @@ def _in_dtype(x):
     return {torch.float32: F32, torch.bfloat16: BF16}[x.dtype]
 
 
-def fp8_quant_act_1x128(x):
-    """x[M][K] f32|bf16 -> (q uint8 [M][K], s float32 [K/128][M])."""
+def fp8_quant_act_1x128(x, pow2=False):
+    """x[M][K] f32|bf16 -> (q uint8 [M][K], s float32 [K/128][M]).
+
+    pow2: power-of-two scales (the E8M0-compatible variant)."""
     if x.dim() != 2:
         raise ValueError("x must be 2-D")
     M, K = x.shape
     px = _dev(x, "x", (torch.float32, torch.bfloat16))
     q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
     s = torch.empty((K // 128 if K % 128 == 0 else 0, M), dtype=torch.float32, device=x.device)
-    _check("fp8_quant_act_1x128",
-           lib().fp8_quant_act_1x128(px, _in_dtype(x), M, K, q.data_ptr(), s.data_ptr(), _stream(x)))
+    fn = "fp8_quant_act_1x128_pow2" if pow2 else "fp8_quant_act_1x128"
+    _check(fn, getattr(lib(), fn)(px, _in_dtype(x), M, K, q.data_ptr(), s.data_ptr(), _stream(x)))
     return q, s
 
 
-def fp8_quant_w_128x128(w, transposed=False):
+def fp8_quant_w_128x128(w, transposed=False, pow2=False):
     """w[N][K] -> (q[N][K], s[N/128][K/128]) and, if transposed, (qT[K][N], sT[K/128][N/128])."""
     if w.dim() != 2:
         raise ValueError("w must be 2-D")
@@ -124,14 +130,14 @@ def fp8_quant_w_128x128(w, transposed=False):
     if transposed:
         qT = torch.empty((K, N), dtype=torch.uint8, device=w.device)
         sT = torch.empty((K // 128, N // 128), dtype=torch.float32, device=w.device)
-    _check("fp8_quant_w_128x128",
-           lib().fp8_quant_w_128x128(pw, _in_dtype(w), N, K, q.data_ptr(), s.data_ptr(),
-                                     qT.data_ptr() if qT is not None else None,
-                                     sT.data_ptr() if sT is not None else None, _stream(w)))
+    fn = "fp8_quant_w_128x128_pow2" if pow2 else "fp8_quant_w_128x128"
+    _check(fn, getattr(lib(), fn)(pw, _in_dtype(w), N, K, q.data_ptr(), s.data_ptr(),
+                                  qT.data_ptr() if qT is not None else None,
+                                  sT.data_ptr() if sT is not None else None, _stream(w)))
     return (q, s, qT, sT) if transposed else (q, s)
 
 
-def fp8_quant_act_128x1_T(x):
+def fp8_quant_act_128x1_T(x, pow2=False):
     """x[M][C] -> (qT uint8 [C][M], sT float32 [M/128][C]); M a multiple of 128."""
     if x.dim() != 2:
         raise ValueError("x must be 2-D")
@@ -139,8 +145,8 @@ def fp8_quant_act_128x1_T(x):
     px = _dev(x, "x", (torch.float32, torch.bfloat16))
     qT = torch.empty((C, M), dtype=torch.uint8, device=x.device)
     sT = torch.empty((M // 128, C), dtype=torch.float32, device=x.device)
-    _check("fp8_quant_act_128x1_T",
-           lib().fp8_quant_act_128x1_T(px, _in_dtype(x), M, C, qT.data_ptr(), sT.data_ptr(), _stream(x)))
+    fn = "fp8_quant_act_128x1_T_pow2" if pow2 else "fp8_quant_act_128x1_T"
+    _check(fn, getattr(lib(), fn)(px, _in_dtype(x), M, C, qT.data_ptr(), sT.data_ptr(), _stream(x)))
     return qT, sT
 
 
@@ -163,16 +169,18 @@ def _gemm_operands(A, sA, B, sB, b_scale_mode):
     return M, N, K, ptrs
 
 
-def fp8_gemm_blockscaled(A, sA, B, sB, b_scale_mode=SCALE_BLOCK128, out=None):
-    """C[M][N] (bf16) = block-scaled FP8 GEMM of A[M][K] and B[N][K] (both K-contiguous)."""
+def fp8_gemm_blockscaled(A, sA, B, sB, b_scale_mode=SCALE_BLOCK128, out=None, pow2=False):
+    """C[M][N] (bf16) = block-scaled FP8 GEMM of A[M][K] and B[N][K] (both K-contiguous).
+
+    pow2: the scales are powers of two and the MFMA applies them (E8M0)."""
     M, N, K, (pa, psa, pb, psb) = _gemm_operands(A, sA, B, sB, b_scale_mode)
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
     pc = _dev(out, "out", (torch.bfloat16,))
     if tuple(out.shape) != (M, N):
         raise ValueError("out has the wrong shape")
-    _check("fp8_gemm_blockscaled",
-           lib().fp8_gemm_blockscaled(pa, psa, pb, psb, int(b_scale_mode), pc, M, N, K, _stream(A)))
+    fn = "fp8_gemm_blockscaled_pow2" if pow2 else "fp8_gemm_blockscaled"
+    _check(fn, getattr(lib(), fn)(pa, psa, pb, psb, int(b_scale_mode), pc, M, N, K, _stream(A)))
     return out
 
 

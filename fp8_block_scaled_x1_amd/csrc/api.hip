@@ -21,6 +21,61 @@ bool valid_dtype(int d) { return d == FP8BS_F32 || d == FP8BS_BF16; }
 
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
+int quant_act_1x128(const void* x, int dtype, bool pow2, int64_t M, int64_t K, uint8_t* q, float* s,
+                    void* stream) {
+  if (!valid_dtype(dtype)) return FP8BS_ERR_DTYPE;
+  if (M < 0 || K < 0 || K % kG) return FP8BS_ERR_SHAPE;
+  // grid: x over groups of 4 chunks, (y, z) over blocks of 8 rows
+  if (K >= kI32 || (M + 7) / 8 >= (int64_t)1 << 27 || (K / kG + 3) / 4 > 65535) return FP8BS_ERR_TOO_LARGE;
+  if (M == 0 || K == 0) return FP8BS_OK;
+  if (!x || !q || !s) return FP8BS_ERR_NULL_PTR;
+  if (misaligned(x) || misaligned(q) || misaligned(s)) return FP8BS_ERR_ALIGN;
+  return status_of(fp8bs::launch_quant_act_1x128(x, dtype == FP8BS_BF16, pow2, M, K, q, s, as_stream(stream)));
+}
+
+int quant_w_128x128(const void* w, int dtype, bool pow2, int64_t N, int64_t K, uint8_t* q, float* s,
+                    uint8_t* qT, float* sT, void* stream) {
+  if (!valid_dtype(dtype)) return FP8BS_ERR_DTYPE;
+  if ((qT == nullptr) != (sT == nullptr)) return FP8BS_ERR_MODE;
+  if (N < 0 || K < 0 || N % kG || K % kG) return FP8BS_ERR_SHAPE;
+  if (N >= kI32 || K >= kI32 || N * K >= kI32 * 4) return FP8BS_ERR_TOO_LARGE;
+  if (N == 0 || K == 0) return FP8BS_OK;
+  if (!w || !q || !s) return FP8BS_ERR_NULL_PTR;
+  if (misaligned(w) || misaligned(q) || misaligned(s) || misaligned(qT) || misaligned(sT))
+    return FP8BS_ERR_ALIGN;
+  if (K / kG > 65535 * 1024 || N / kG > 65535) return FP8BS_ERR_TOO_LARGE;
+  return status_of(fp8bs::launch_quant_w_128x128(w, dtype == FP8BS_BF16, pow2, N, K, q, s, qT, sT,
+                                                 as_stream(stream)));
+}
+
+int quant_act_128x1_T(const void* x, int dtype, bool pow2, int64_t M, int64_t C, uint8_t* qT, float* sT,
+                      void* stream) {
+  if (!valid_dtype(dtype)) return FP8BS_ERR_DTYPE;
+  if (M < 0 || C < 0 || M % kG) return FP8BS_ERR_SHAPE;
+  if (M >= kI32 || C >= kI32 || M / kG > 65535) return FP8BS_ERR_TOO_LARGE;
+  if (M == 0 || C == 0) return FP8BS_OK;
+  if (!x || !qT || !sT) return FP8BS_ERR_NULL_PTR;
+  if (misaligned(x) || misaligned(qT) || misaligned(sT)) return FP8BS_ERR_ALIGN;
+  return status_of(fp8bs::launch_quant_act_128x1_T(x, dtype == FP8BS_BF16, pow2, M, C, qT, sT,
+                                                   as_stream(stream)));
+}
+
+int gemm_blockscaled(const uint8_t* A, const float* sA, const uint8_t* B, const float* sB, int b_scale_mode,
+                     uint16_t* C, int64_t M, int64_t N, int64_t K, bool pow2, void* stream) {
+  if (b_scale_mode != FP8BS_SCALE_BLOCK128 && b_scale_mode != FP8BS_SCALE_ROW) return FP8BS_ERR_MODE;
+  if (M < 0 || N < 0 || K <= 0 || K % kG || N % kG) return FP8BS_ERR_SHAPE;
+  if (M * K >= kI32 || N * K >= kI32 || M * N >= kI32) return FP8BS_ERR_TOO_LARGE;
+  if (M == 0 || N == 0) return FP8BS_OK;
+  if (!A || !sA || !B || !sB || !C) return FP8BS_ERR_NULL_PTR;
+  if (misaligned(A) || misaligned(sA) || misaligned(B) || misaligned(sB) || misaligned(C))
+    return FP8BS_ERR_ALIGN;
+  if (pow2)
+    return status_of(fp8bs::launch_gemm_blockscaled_pow2(A, sA, B, sB, b_scale_mode, C, M, N, K,
+                                                         as_stream(stream)));
+  return status_of(fp8bs::launch_gemm_blockscaled(A, sA, B, sB, b_scale_mode, C, M, N, K,
+                                                  as_stream(stream)));
+}
+
 }  // namespace
 
 extern "C" {
@@ -43,55 +98,44 @@ const char* fp8bs_status_string(int status) {
 
 int fp8_quant_act_1x128(const void* x, int dtype, int64_t M, int64_t K, uint8_t* q, float* s,
                         void* stream) {
-  if (!valid_dtype(dtype)) return FP8BS_ERR_DTYPE;
-  if (M < 0 || K < 0 || K % kG) return FP8BS_ERR_SHAPE;
-  // grid: x over groups of 4 chunks, (y, z) over blocks of 8 rows
-  if (K >= kI32 || (M + 7) / 8 >= (int64_t)1 << 27 || (K / kG + 3) / 4 > 65535) return FP8BS_ERR_TOO_LARGE;
-  if (M == 0 || K == 0) return FP8BS_OK;
-  if (!x || !q || !s) return FP8BS_ERR_NULL_PTR;
-  if (misaligned(x) || misaligned(q) || misaligned(s)) return FP8BS_ERR_ALIGN;
-  return status_of(fp8bs::launch_quant_act_1x128(x, dtype == FP8BS_BF16, M, K, q, s, as_stream(stream)));
+  return quant_act_1x128(x, dtype, false, M, K, q, s, stream);
+}
+
+int fp8_quant_act_1x128_pow2(const void* x, int dtype, int64_t M, int64_t K, uint8_t* q, float* s,
+                             void* stream) {
+  return quant_act_1x128(x, dtype, true, M, K, q, s, stream);
 }
 
 int fp8_quant_w_128x128(const void* w, int dtype, int64_t N, int64_t K, uint8_t* q, float* s,
                         uint8_t* qT, float* sT, void* stream) {
-  if (!valid_dtype(dtype)) return FP8BS_ERR_DTYPE;
-  if ((qT == nullptr) != (sT == nullptr)) return FP8BS_ERR_MODE;
-  if (N < 0 || K < 0 || N % kG || K % kG) return FP8BS_ERR_SHAPE;
-  if (N >= kI32 || K >= kI32 || N * K >= kI32 * 4) return FP8BS_ERR_TOO_LARGE;
-  if (N == 0 || K == 0) return FP8BS_OK;
-  if (!w || !q || !s) return FP8BS_ERR_NULL_PTR;
-  if (misaligned(w) || misaligned(q) || misaligned(s) || misaligned(qT) || misaligned(sT))
-    return FP8BS_ERR_ALIGN;
-  if (K / kG > 65535 * 1024 || N / kG > 65535) return FP8BS_ERR_TOO_LARGE;
-  return status_of(fp8bs::launch_quant_w_128x128(w, dtype == FP8BS_BF16, N, K, q, s, qT, sT,
-                                                 as_stream(stream)));
+  return quant_w_128x128(w, dtype, false, N, K, q, s, qT, sT, stream);
+}
+
+int fp8_quant_w_128x128_pow2(const void* w, int dtype, int64_t N, int64_t K, uint8_t* q, float* s,
+                             uint8_t* qT, float* sT, void* stream) {
+  return quant_w_128x128(w, dtype, true, N, K, q, s, qT, sT, stream);
 }
 
 int fp8_quant_act_128x1_T(const void* x, int dtype, int64_t M, int64_t C, uint8_t* qT, float* sT,
                           void* stream) {
-  if (!valid_dtype(dtype)) return FP8BS_ERR_DTYPE;
-  if (M < 0 || C < 0 || M % kG) return FP8BS_ERR_SHAPE;
-  if (M >= kI32 || C >= kI32 || M / kG > 65535) return FP8BS_ERR_TOO_LARGE;
-  if (M == 0 || C == 0) return FP8BS_OK;
-  if (!x || !qT || !sT) return FP8BS_ERR_NULL_PTR;
-  if (misaligned(x) || misaligned(qT) || misaligned(sT)) return FP8BS_ERR_ALIGN;
-  return status_of(fp8bs::launch_quant_act_128x1_T(x, dtype == FP8BS_BF16, M, C, qT, sT,
-                                                   as_stream(stream)));
+  return quant_act_128x1_T(x, dtype, false, M, C, qT, sT, stream);
+}
+
+int fp8_quant_act_128x1_T_pow2(const void* x, int dtype, int64_t M, int64_t C, uint8_t* qT, float* sT,
+                               void* stream) {
+  return quant_act_128x1_T(x, dtype, true, M, C, qT, sT, stream);
 }
 
 int fp8_gemm_blockscaled(const uint8_t* A, const float* sA, const uint8_t* B, const float* sB,
                          int b_scale_mode, uint16_t* C, int64_t M, int64_t N, int64_t K,
                          void* stream) {
-  if (b_scale_mode != FP8BS_SCALE_BLOCK128 && b_scale_mode != FP8BS_SCALE_ROW) return FP8BS_ERR_MODE;
-  if (M < 0 || N < 0 || K <= 0 || K % kG || N % kG) return FP8BS_ERR_SHAPE;
-  if (M * K >= kI32 || N * K >= kI32 || M * N >= kI32) return FP8BS_ERR_TOO_LARGE;
-  if (M == 0 || N == 0) return FP8BS_OK;
-  if (!A || !sA || !B || !sB || !C) return FP8BS_ERR_NULL_PTR;
-  if (misaligned(A) || misaligned(sA) || misaligned(B) || misaligned(sB) || misaligned(C))
-    return FP8BS_ERR_ALIGN;
-  return status_of(fp8bs::launch_gemm_blockscaled(A, sA, B, sB, b_scale_mode, C, M, N, K,
-                                                  as_stream(stream)));
+  return gemm_blockscaled(A, sA, B, sB, b_scale_mode, C, M, N, K, false, stream);
+}
+
+int fp8_gemm_blockscaled_pow2(const uint8_t* A, const float* sA, const uint8_t* B, const float* sB,
+                              int b_scale_mode, uint16_t* C, int64_t M, int64_t N, int64_t K,
+                              void* stream) {
+  return gemm_blockscaled(A, sA, B, sB, b_scale_mode, C, M, N, K, true, stream);
 }
 
 int fp8_gemm_blockscaled_q1x128(const uint8_t* A, const float* sA, const uint8_t* B,

@@ -185,6 +185,52 @@ __device__ __forceinline__ uint32_t e4m3_div_pack4_t(float x0, float x1, float x
     return e4m3_div_pack4(x0, x1, x2, x3, g.s, g.r, g.fast);
 }
 
+// ---------------------------------------------------------------------------
+// Power-of-two scales (the E8M0-compatible variant): the scale is the smallest
+// power of two not below RN(amax / 448), and not below 2^-126 (a normal FP32,
+// so its exponent field is its E8M0 encoding); a zero group keeps 1.0. The
+// codes are then E4M3(x * 2^-e): a product with a power of two is exact
+// wherever it is a normal number, and below that the code is +-0 either way.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float pow2_scale(float amax) {
+  const uint32_t b = __float_as_uint(group_scale(amax));
+  return __uint_as_float((b + 0x7FFFFFu) & 0xFF800000u);
+}
+// 1/s for a power-of-two s = 2^(E-127), E in [1, 253]: exponent field 254 - E
+__device__ __forceinline__ float pow2_recip(float s) { return __uint_as_float((254u << 23) - __float_as_uint(s)); }
+
+// The quantizers' scale rule: POW2 selects the power-of-two variant.
+template <bool POW2>
+__device__ __forceinline__ float scale_rule(float amax) {
+  if constexpr (POW2)
+    return pow2_scale(amax);
+  else
+    return group_scale(amax);
+}
+template <bool BF16, bool POW2>
+__device__ __forceinline__ GroupDiv div_of_scale_rule(float s) {
+  if constexpr (POW2) {
+    GroupDiv g;
+    g.s = s;
+    g.r = pow2_recip(s);
+    g.fast = true;
+    return g;
+  } else {
+    return group_div_of_scale<BF16>(s);
+  }
+}
+template <bool BF16, bool POW2>
+__device__ __forceinline__ GroupDiv div_rule(float amax) {
+  return div_of_scale_rule<BF16, POW2>(scale_rule<POW2>(amax));
+}
+template <bool BF16, bool POW2>
+__device__ __forceinline__ uint32_t pack4_rule(float x0, float x1, float x2, float x3, const GroupDiv& g) {
+  if constexpr (POW2)
+    return e4m3_pack4(x0 * g.r, x1 * g.r, x2 * g.r, x3 * g.r);
+  else
+    return e4m3_div_pack4_t<BF16>(x0, x1, x2, x3, g);
+}
+
 // Max over the 16 lanes of a DPP row (lanes 16r..16r+15), result in every lane
 // of the row. row_ror rotates within the row.
 __device__ __forceinline__ float row16_max(float v) {

@@ -187,7 +187,11 @@ __device__ __forceinline__ void wait_and_barrier() {
 // QOUT: the epilogue writes the 1x128 quantization (E4M3 codes and FP32
 // scales per row and 128 columns) of the BF16-rounded result instead of the
 // BF16 result itself.
-template <class G, int ROW_MODE, int QOUT = 0>
+// HW: the scales are powers of two and the MFMA applies them itself, as E8M0
+// block scales of its operands (the exponent field of an FP32 power of two is
+// its E8M0 code); each MFMA then accumulates straight into the FP32
+// accumulator and no promotion FMAs run.
+template <class G, int ROW_MODE, int QOUT = 0, int HW = 0>
 __device__ __forceinline__ void run_tile(const Tile& t, uint8_t* smem) {
   constexpr int MS = G::MS, NS = G::NS, WM = G::WM, WN = G::WN;
   constexpr bool kDeepA = G::DA == 3, kDeepB = G::DB == 3, kDeep = kDeepA || kDeepB;
@@ -487,7 +491,59 @@ __device__ __forceinline__ void run_tile(const Tile& t, uint8_t* smem) {
     }
     if constexpr (kCarry) promote_step(NT - 1, p_prev, sc, f_prev, S);
   };
-  if constexpr (ROW_MODE || (G::BN % BK == 0 && BK % WN == 0)) {
+  // Hardware-scaled main loop. MFMA operand lane l holds row l%16 of its
+  // 16-row subtile (and 32 K bytes of it), and its E8M0 scale operand is that
+  // row's scale for those 32 K values; with 128-wide groups all four lanes of
+  // a row carry the same scale. src0 = B rows (scale sb of column n), src1 =
+  // A rows (scale sa of row m).
+  auto read_scales_hw = [&](int kb, int (&ea)[MS], int (&eb)[NS]) {
+    const float* sAs = reinterpret_cast<const float*>(slot_a(kb) + G::BM * BK) + wm * WM + (lane & 15);
+#pragma unroll
+    for (int i = 0; i < MS; ++i) ea[i] = (int)(__float_as_uint(sAs[16 * i]) >> 23);
+    if constexpr (ROW_MODE) {
+      const float* sBs = reinterpret_cast<const float*>(slot_b(kb) + G::BN * BK) + wn * WN + (lane & 15);
+#pragma unroll
+      for (int j = 0; j < NS; ++j) eb[j] = (int)(__float_as_uint(sBs[16 * j]) >> 23);
+    } else {
+      const int elo = (int)(__float_as_uint(sbb_lo[kb]) >> 23), ehi = (int)(__float_as_uint(sbb_hi[kb]) >> 23);
+#pragma unroll
+      for (int j = 0; j < NS; ++j) eb[j] = j < split ? elo : ehi;
+    }
+  };
+  auto main_loop_hw = [&]() {
+    v8i hf[NH];
+    v8i tf;
+    int ea[MS], eb[NS];
+#pragma unroll
+    for (int h = 0; h < NH; ++h) hf[h] = read_frag(HA ? slot_a(0) : slot_b(0), h_sub + h, lane);
+    tf = read_t(0, 0);
+    read_scales_hw(0, ea, eb);
+    for (int kb = 0; kb < nkb; ++kb) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        refill_step(t, kb);
+        const v8i t_now = tf;
+#pragma unroll
+        for (int h = 0; h < NH; ++h) {
+          const int i = HA ? h : t, j = HA ? t : h;
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(HA ? t_now : hf[h], HA ? hf[h] : t_now,
+                                                                       acc[i][j], 0, 0, 0, eb[j], 0, ea[i]);
+        }
+        if (t + 1 < NT) tf = read_t(kb, t + 1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      barrier(kb + 1);
+      const int kn = min(kb + 1, nkb - 1);
+#pragma unroll
+      for (int h = 0; h < NH; ++h) hf[h] = read_frag(HA ? slot_a(kn) : slot_b(kn), h_sub + h, lane);
+      tf = read_t(kn, 0);
+      read_scales_hw(kn, ea, eb);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  if constexpr (HW) {
+    main_loop_hw();
+  } else if constexpr (ROW_MODE || (G::BN % BK == 0 && BK % WN == 0)) {
     main_loop(std::integral_constant<int, NS>{});   // every wave within one block
   } else {
     switch (split) {
@@ -586,7 +642,7 @@ __device__ __forceinline__ void run_tile(const Tile& t, uint8_t* smem) {
   }
 }
 
-template <class G, int ROW_MODE, int QOUT>
+template <class G, int ROW_MODE, int QOUT, int HW = 0>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const uint8_t* __restrict__ A,
                                                             const float* __restrict__ sA,
                                                             const uint8_t* __restrict__ B,
@@ -605,7 +661,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const uint8_t* __rest
   t.B = B; t.sB = sB; t.C = C; t.Q = Q; t.sQ = sQ;
   t.m0 = tm * G::BM; t.row_end = M;
   t.n0 = tn * G::BN; t.N = N; t.K = K; t.ld = K;
-  run_tile<G, ROW_MODE, QOUT>(t, smem);
+  run_tile<G, ROW_MODE, QOUT, HW>(t, smem);
 }
 
 // Per-expert tiles: expert e owns rows [off[e], off[e+1]); its tiles are
@@ -716,16 +772,16 @@ int pick_dense(int64_t M, int64_t N) {
   return c1 <= c2 ? 1 : 2;
 }
 
-template <class G, int QOUT>
+template <class G, int QOUT, int HW = 0>
 hipError_t launch_dense(const uint8_t* A, const float* sA, const uint8_t* B, const float* sB,
                         int row_mode, uint16_t* C, uint8_t* Q, float* sQ, int64_t M, int64_t N,
                         int64_t K, hipStream_t stream) {
   const int tiles = (int)(((M + G::BM - 1) / G::BM) * ((N + G::BN - 1) / G::BN));
   if (row_mode)
-    hipLaunchKernelGGL((gemm_kernel<G, 1, QOUT>), dim3(tiles), dim3(kThreads), 0, stream, A, sA, B, sB,
+    hipLaunchKernelGGL((gemm_kernel<G, 1, QOUT, HW>), dim3(tiles), dim3(kThreads), 0, stream, A, sA, B, sB,
                        C, Q, sQ, (int)M, (int)N, (int)K);
   else
-    hipLaunchKernelGGL((gemm_kernel<G, 0, QOUT>), dim3(tiles), dim3(kThreads), 0, stream, A, sA, B, sB,
+    hipLaunchKernelGGL((gemm_kernel<G, 0, QOUT, HW>), dim3(tiles), dim3(kThreads), 0, stream, A, sA, B, sB,
                        C, Q, sQ, (int)M, (int)N, (int)K);
   return hipGetLastError();
 }
@@ -740,6 +796,17 @@ hipError_t launch_gemm_blockscaled(const uint8_t* A, const float* sA, const uint
     case 1: return launch_dense<Cfg256x224, 0>(A, sA, B, sB, row_mode, C, nullptr, nullptr, M, N, K, stream);
     case 2: return launch_dense<Cfg224x256, 0>(A, sA, B, sB, row_mode, C, nullptr, nullptr, M, N, K, stream);
     default: return launch_dense<Cfg256x256, 0>(A, sA, B, sB, row_mode, C, nullptr, nullptr, M, N, K, stream);
+  }
+}
+
+hipError_t launch_gemm_blockscaled_pow2(const uint8_t* A, const float* sA, const uint8_t* B,
+                                        const float* sB, int row_mode, uint16_t* C, int64_t M,
+                                        int64_t N, int64_t K, hipStream_t stream) {
+  using namespace gemm;
+  switch (pick_dense(M, N)) {
+    case 1: return launch_dense<Cfg256x224, 0, 1>(A, sA, B, sB, row_mode, C, nullptr, nullptr, M, N, K, stream);
+    case 2: return launch_dense<Cfg224x256, 0, 1>(A, sA, B, sB, row_mode, C, nullptr, nullptr, M, N, K, stream);
+    default: return launch_dense<Cfg256x256, 0, 1>(A, sA, B, sB, row_mode, C, nullptr, nullptr, M, N, K, stream);
   }
 }
 

@@ -7,15 +7,20 @@
 
 namespace fp8bs {
 
-hipError_t launch_quant_act_1x128(const void* x, bool bf16, int64_t M, int64_t K, uint8_t* q,
+// pow2: power-of-two scales (the E8M0-compatible variant) instead of amax / 448
+hipError_t launch_quant_act_1x128(const void* x, bool bf16, bool pow2, int64_t M, int64_t K, uint8_t* q,
                                   float* s, hipStream_t stream);
-hipError_t launch_quant_w_128x128(const void* w, bool bf16, int64_t N, int64_t K, uint8_t* q,
+hipError_t launch_quant_w_128x128(const void* w, bool bf16, bool pow2, int64_t N, int64_t K, uint8_t* q,
                                   float* s, uint8_t* qT, float* sT, hipStream_t stream);
-hipError_t launch_quant_act_128x1_T(const void* x, bool bf16, int64_t M, int64_t C, uint8_t* qT,
+hipError_t launch_quant_act_128x1_T(const void* x, bool bf16, bool pow2, int64_t M, int64_t C, uint8_t* qT,
                                     float* sT, hipStream_t stream);
 hipError_t launch_gemm_blockscaled(const uint8_t* A, const float* sA, const uint8_t* B,
                                    const float* sB, int row_mode, uint16_t* C, int64_t M,
                                    int64_t N, int64_t K, hipStream_t stream);
+// sA and sB hold powers of two; the MFMA applies them as E8M0 block scales
+hipError_t launch_gemm_blockscaled_pow2(const uint8_t* A, const float* sA, const uint8_t* B,
+                                        const float* sB, int row_mode, uint16_t* C, int64_t M,
+                                        int64_t N, int64_t K, hipStream_t stream);
 hipError_t launch_gemm_blockscaled_q1x128(const uint8_t* A, const float* sA, const uint8_t* B,
                                           const float* sB, int row_mode, uint8_t* Q, float* sQ,
                                           int64_t M, int64_t N, int64_t K, hipStream_t stream);

@@ -16,6 +16,8 @@
 //                     transposed (the pages call a transposition fused into
 //                     the GEMM cumbersome, report section 3.5.2)  sT[M/128][C]
 
+#include <type_traits>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -43,10 +45,10 @@ __device__ __forceinline__ void load8(const void* base, int64_t elem, float v[8]
 }
 
 // codes of v[i] / s (IEEE FP32 division, then E4M3)
-template <bool BF16>
+template <bool BF16, bool POW2>
 __device__ __forceinline__ uint2 cast8(const float v[8], const GroupDiv& g) {
-  return make_uint2(e4m3_div_pack4_t<BF16>(v[0], v[1], v[2], v[3], g),
-                    e4m3_div_pack4_t<BF16>(v[4], v[5], v[6], v[7], g));
+  return make_uint2(pack4_rule<BF16, POW2>(v[0], v[1], v[2], v[3], g),
+                    pack4_rule<BF16, POW2>(v[4], v[5], v[6], v[7], g));
 }
 
 // ---------------------------------------------------------------------------
@@ -62,7 +64,7 @@ __device__ __forceinline__ uint2 cast8(const float v[8], const GroupDiv& g) {
 // ---------------------------------------------------------------------------
 constexpr int kActRows = 2;   // rows per wave
 
-template <bool BF16>
+template <bool BF16, bool POW2>
 __global__ __launch_bounds__(256) void quant_act_1x128_kernel(
     const void* __restrict__ x, int64_t M, int K, uint8_t* __restrict__ q,
     float* __restrict__ s) {
@@ -88,8 +90,8 @@ __global__ __launch_bounds__(256) void quant_act_1x128_kernel(
 #pragma unroll
     for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[u][i]));
     amax = row16_max(amax);
-    const GroupDiv g = group_div<BF16>(amax);
-    const uint2 codes = cast8<BF16>(v[u], g);
+    const GroupDiv g = div_rule<BF16, POW2>(amax);
+    const uint2 codes = cast8<BF16, POW2>(v[u], g);
     const int64_t row = row0 + u;
     if (row < M && kb < nkb) {
       *reinterpret_cast<uint2*>(q + row * K + (int64_t)kb * kGroup + part * 8) = codes;
@@ -107,7 +109,7 @@ __global__ __launch_bounds__(256) void quant_act_1x128_kernel(
 // ---------------------------------------------------------------------------
 constexpr int kTileStride = kGroup + 4;   // LDS row pitch in bytes (padding against bank conflicts)
 
-template <bool BF16, bool TRANS>
+template <bool BF16, bool TRANS, bool POW2>
 __global__ __launch_bounds__(256) void quant_w_128x128_kernel(
     const void* __restrict__ w, int N, int K, uint8_t* __restrict__ q, float* __restrict__ s,
     uint8_t* __restrict__ qT, float* __restrict__ sT) {
@@ -133,13 +135,13 @@ __global__ __launch_bounds__(256) void quant_w_128x128_kernel(
   if ((t & 63) == 0) red[t >> 6] = amax;
   __syncthreads();
   amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  const GroupDiv g = group_div<BF16>(amax);
+  const GroupDiv g = div_rule<BF16, POW2>(amax);
   const float sc = g.s;
 
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int rl = i * 16 + r0;
-    const uint2 codes = cast8<BF16>(v[i], g);
+    const uint2 codes = cast8<BF16, POW2>(v[i], g);
     *reinterpret_cast<uint2*>(q + ((int64_t)nb * kGroup + rl) * K + (int64_t)kb * kGroup + part * 8) = codes;
     if constexpr (TRANS) {
       uint32_t* d = reinterpret_cast<uint32_t*>(tile + rl * kTileStride + part * 8);
@@ -183,7 +185,7 @@ __global__ __launch_bounds__(256) void quant_w_128x128_kernel(
 // combined across the 8 token slices through LDS; each thread then writes its
 // 16 codes per channel as one 16-byte piece of a qT row.
 // ---------------------------------------------------------------------------
-template <bool BF16, bool PAIR>
+template <bool BF16, bool PAIR, bool POW2>
 __global__ __launch_bounds__(256) void quant_act_128x1_T_kernel(
     const void* __restrict__ x, int64_t M, int C, uint8_t* __restrict__ qT, float* __restrict__ sT) {
   __shared__ float red[8][64];
@@ -240,17 +242,18 @@ __global__ __launch_bounds__(256) void quant_act_128x1_T_kernel(
     float amax = red[0][t];
 #pragma unroll
     for (int g = 1; g < 8; ++g) amax = fmaxf(amax, red[g][t]);
-    const float sc = group_scale(amax);
+    const float sc = scale_rule<POW2>(amax);
     scl[t] = sc;
     if (c0 + t < C) sT[(int64_t)tb * C + c0 + t] = sc;
   }
   __syncthreads();
-  const GroupDiv g0 = group_div_of_scale<BF16>(scl[2 * cp]), g1 = group_div_of_scale<BF16>(scl[2 * cp + 1]);
+  const GroupDiv g0 = div_of_scale_rule<BF16, POW2>(scl[2 * cp]);
+  const GroupDiv g1 = div_of_scale_rule<BF16, POW2>(scl[2 * cp + 1]);
   uint32_t w0[4], w1[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    w0[j] = e4m3_div_pack4_t<BF16>(v0[4 * j], v0[4 * j + 1], v0[4 * j + 2], v0[4 * j + 3], g0);
-    w1[j] = e4m3_div_pack4_t<BF16>(v1[4 * j], v1[4 * j + 1], v1[4 * j + 2], v1[4 * j + 3], g1);
+    w0[j] = pack4_rule<BF16, POW2>(v0[4 * j], v0[4 * j + 1], v0[4 * j + 2], v0[4 * j + 3], g0);
+    w1[j] = pack4_rule<BF16, POW2>(v1[4 * j], v1[4 * j + 1], v1[4 * j + 2], v1[4 * j + 3], g1);
   }
   if (ok0) *reinterpret_cast<uint4*>(qT + (int64_t)ch * M + tok0) = make_uint4(w0[0], w0[1], w0[2], w0[3]);
   if (ok1) *reinterpret_cast<uint4*>(qT + (int64_t)(ch + 1) * M + tok0) = make_uint4(w1[0], w1[1], w1[2], w1[3]);
@@ -276,7 +279,7 @@ __global__ __launch_bounds__(256) void quant_act_128x1_T_kernel(
 // ---------------------------------------------------------------------------
 constexpr int kTPitch = kGroup + 16;   // tile row pitch in bytes (16-byte aligned)
 
-template <bool BF16, bool GROUPED>
+template <bool BF16, bool GROUPED, bool POW2>
 __global__ __launch_bounds__(256) void quant_act_128x1_T_v8_kernel(
     const void* __restrict__ x, int64_t M, int C, uint8_t* __restrict__ qT, float* __restrict__ sT,
     const int32_t* __restrict__ off, int E, int64_t ld) {
@@ -319,16 +322,16 @@ __global__ __launch_bounds__(256) void quant_act_128x1_T_v8_kernel(
     float amax = red[0][t];
 #pragma unroll
     for (int r = 1; r < 32; ++r) amax = fmaxf(amax, red[r][t]);
-    const float sc = group_scale(amax);
+    const float sc = scale_rule<POW2>(amax);
     scl[t] = sc;
     if (c0 + t < C) sT[(int64_t)g * C + c0 + t] = sc;
   }
   __syncthreads();
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const GroupDiv gd = group_div_of_scale<BF16>(scl[8 * cg + j]);
+    const GroupDiv gd = div_of_scale_rule<BF16, POW2>(scl[8 * cg + j]);
     *reinterpret_cast<uint32_t*>(tile + (8 * cg + j) * kTPitch + tl) =
-        e4m3_div_pack4_t<BF16>(v[0][j], v[1][j], v[2][j], v[3][j], gd);
+        pack4_rule<BF16, POW2>(v[0][j], v[1][j], v[2][j], v[3][j], gd);
   }
   __syncthreads();
 #pragma unroll
@@ -344,55 +347,59 @@ __global__ __launch_bounds__(256) void quant_act_128x1_T_v8_kernel(
 // ---------------------------------------------------------------------------
 // Launchers (shapes validated by the C ABI layer).
 // ---------------------------------------------------------------------------
-hipError_t launch_quant_act_1x128(const void* x, bool bf16, int64_t M, int64_t K, uint8_t* q,
+hipError_t launch_quant_act_1x128(const void* x, bool bf16, bool pow2, int64_t M, int64_t K, uint8_t* q,
                                   float* s, hipStream_t stream) {
   const int64_t nkb = K / kGroup;
   const int64_t nrb = (M + 4 * kActRows - 1) / (4 * kActRows);
   const int64_t gy = nrb < 65535 ? nrb : 65535;
   const dim3 grid((unsigned)((nkb + 3) / 4), (unsigned)gy, (unsigned)((nrb + gy - 1) / gy));
-  if (bf16)
-    hipLaunchKernelGGL(quant_act_1x128_kernel<true>, grid, dim3(256), 0, stream, x, M, (int)K, q, s);
-  else
-    hipLaunchKernelGGL(quant_act_1x128_kernel<false>, grid, dim3(256), 0, stream, x, M, (int)K, q, s);
+  auto go = [&](auto bf, auto p2) {
+    hipLaunchKernelGGL((quant_act_1x128_kernel<decltype(bf)::value, decltype(p2)::value>), grid, dim3(256), 0,
+                       stream, x, M, (int)K, q, s);
+  };
+  using T = std::true_type;
+  using F = std::false_type;
+  if (bf16) pow2 ? go(T{}, T{}) : go(T{}, F{});
+  else pow2 ? go(F{}, T{}) : go(F{}, F{});
   return hipGetLastError();
 }
 
-hipError_t launch_quant_w_128x128(const void* w, bool bf16, int64_t N, int64_t K, uint8_t* q,
+hipError_t launch_quant_w_128x128(const void* w, bool bf16, bool pow2, int64_t N, int64_t K, uint8_t* q,
                                   float* s, uint8_t* qT, float* sT, hipStream_t stream) {
   const dim3 grid((unsigned)(K / kGroup), (unsigned)(N / kGroup));
-  const bool tr = qT != nullptr;
-  if (bf16 && tr)
-    hipLaunchKernelGGL((quant_w_128x128_kernel<true, true>), grid, dim3(256), 0, stream, w, (int)N, (int)K, q, s, qT, sT);
-  else if (bf16)
-    hipLaunchKernelGGL((quant_w_128x128_kernel<true, false>), grid, dim3(256), 0, stream, w, (int)N, (int)K, q, s, qT, sT);
-  else if (tr)
-    hipLaunchKernelGGL((quant_w_128x128_kernel<false, true>), grid, dim3(256), 0, stream, w, (int)N, (int)K, q, s, qT, sT);
-  else
-    hipLaunchKernelGGL((quant_w_128x128_kernel<false, false>), grid, dim3(256), 0, stream, w, (int)N, (int)K, q, s, qT, sT);
+  auto go = [&](auto bf, auto tr, auto p2) {
+    hipLaunchKernelGGL((quant_w_128x128_kernel<decltype(bf)::value, decltype(tr)::value, decltype(p2)::value>),
+                       grid, dim3(256), 0, stream, w, (int)N, (int)K, q, s, qT, sT);
+  };
+  using T = std::true_type;
+  using F = std::false_type;
+  auto with_tr = [&](auto bf, auto p2) { qT != nullptr ? go(bf, T{}, p2) : go(bf, F{}, p2); };
+  if (bf16) pow2 ? with_tr(T{}, T{}) : with_tr(T{}, F{});
+  else pow2 ? with_tr(F{}, T{}) : with_tr(F{}, F{});
   return hipGetLastError();
 }
 
-hipError_t launch_quant_act_128x1_T(const void* x, bool bf16, int64_t M, int64_t C, uint8_t* qT,
+hipError_t launch_quant_act_128x1_T(const void* x, bool bf16, bool pow2, int64_t M, int64_t C, uint8_t* qT,
                                     float* sT, hipStream_t stream) {
   const dim3 grid((unsigned)((C + 63) / 64), (unsigned)(M / kGroup));
+  using T = std::true_type;
+  using F = std::false_type;
   if (C % 8 == 0) {
-    if (bf16)
-      hipLaunchKernelGGL((quant_act_128x1_T_v8_kernel<true, false>), grid, dim3(256), 0, stream, x, M, (int)C,
-                         qT, sT, nullptr, 0, M);
-    else
-      hipLaunchKernelGGL((quant_act_128x1_T_v8_kernel<false, false>), grid, dim3(256), 0, stream, x, M, (int)C,
-                         qT, sT, nullptr, 0, M);
+    auto go = [&](auto bf, auto p2) {
+      hipLaunchKernelGGL((quant_act_128x1_T_v8_kernel<decltype(bf)::value, false, decltype(p2)::value>), grid,
+                         dim3(256), 0, stream, x, M, (int)C, qT, sT, nullptr, 0, M);
+    };
+    if (bf16) pow2 ? go(T{}, T{}) : go(T{}, F{});
+    else pow2 ? go(F{}, T{}) : go(F{}, F{});
     return hipGetLastError();
   }
-  const bool pair = (C % 2) == 0;
-  if (bf16 && pair)
-    hipLaunchKernelGGL((quant_act_128x1_T_kernel<true, true>), grid, dim3(256), 0, stream, x, M, (int)C, qT, sT);
-  else if (bf16)
-    hipLaunchKernelGGL((quant_act_128x1_T_kernel<true, false>), grid, dim3(256), 0, stream, x, M, (int)C, qT, sT);
-  else if (pair)
-    hipLaunchKernelGGL((quant_act_128x1_T_kernel<false, true>), grid, dim3(256), 0, stream, x, M, (int)C, qT, sT);
-  else
-    hipLaunchKernelGGL((quant_act_128x1_T_kernel<false, false>), grid, dim3(256), 0, stream, x, M, (int)C, qT, sT);
+  auto go = [&](auto bf, auto pair, auto p2) {
+    hipLaunchKernelGGL((quant_act_128x1_T_kernel<decltype(bf)::value, decltype(pair)::value, decltype(p2)::value>),
+                       grid, dim3(256), 0, stream, x, M, (int)C, qT, sT);
+  };
+  auto with_pair = [&](auto bf, auto p2) { (C % 2) == 0 ? go(bf, T{}, p2) : go(bf, F{}, p2); };
+  if (bf16) pow2 ? with_pair(T{}, T{}) : with_pair(T{}, F{});
+  else pow2 ? with_pair(F{}, T{}) : with_pair(F{}, F{});
   return hipGetLastError();
 }
 
@@ -402,11 +409,11 @@ hipError_t launch_quant_act_128x1_T_grouped(const void* x, bool bf16, int64_t M_
   // ld / 128 bounds the number of groups (validated: ld >= M_total + 127 E)
   const dim3 grid((unsigned)((C + 63) / 64), (unsigned)(ld / kGroup));
   if (bf16)
-    hipLaunchKernelGGL((quant_act_128x1_T_v8_kernel<true, true>), grid, dim3(256), 0, stream, x, M_total, (int)C,
-                       qT, sT, offsets, E, ld);
+    hipLaunchKernelGGL((quant_act_128x1_T_v8_kernel<true, true, false>), grid, dim3(256), 0, stream, x, M_total,
+                       (int)C, qT, sT, offsets, E, ld);
   else
-    hipLaunchKernelGGL((quant_act_128x1_T_v8_kernel<false, true>), grid, dim3(256), 0, stream, x, M_total, (int)C,
-                       qT, sT, offsets, E, ld);
+    hipLaunchKernelGGL((quant_act_128x1_T_v8_kernel<false, true, false>), grid, dim3(256), 0, stream, x, M_total,
+                       (int)C, qT, sT, offsets, E, ld);
   return hipGetLastError();
 }
 

@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define FP8BS_ABI_VERSION 4
+#define FP8BS_ABI_VERSION 5
 
 #ifndef FP8BS_API
 #define FP8BS_API __attribute__((visibility("default")))
@@ -126,6 +126,37 @@ FP8BS_API int fp8_quant_act_128x1_T(const void* x, int dtype, int64_t M, int64_t
  * K and N multiples of 128; any M >= 0. M*K, N*K and M*N below 2^31.
  */
 FP8BS_API int fp8_gemm_blockscaled(const uint8_t* A, const float* sA, const uint8_t* B,
+                         const float* sB, int b_scale_mode, uint16_t* C,
+                         int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
+ * Power-of-two scale variant (report section 3.5.2 on the innerforce.co.kr
+ * page wishes for dequantization inside the matrix unit; gfx950's MFMA can
+ * apply E8M0 block scales, i.e. powers of two, to its operands itself). The
+ * quantizers below are fp8_quant_act_1x128, fp8_quant_w_128x128 and
+ * fp8_quant_act_128x1_T with one change: each group's scale is the smallest
+ * power of two not below amax/448 (the FP32 quotient), and not below 2^-126;
+ * 1.0 for a zero group. Codes are E4M3(x / s), exact scaling by a power of
+ * two. Layouts, arguments and errors as for the corresponding entry point.
+ */
+FP8BS_API int fp8_quant_act_1x128_pow2(const void* x, int dtype, int64_t M, int64_t K,
+                        uint8_t* q, float* s, void* stream);
+FP8BS_API int fp8_quant_w_128x128_pow2(const void* w, int dtype, int64_t N, int64_t K,
+                        uint8_t* q, float* s, uint8_t* qT, float* sT,
+                        void* stream);
+FP8BS_API int fp8_quant_act_128x1_T_pow2(const void* x, int dtype, int64_t M, int64_t C,
+                          uint8_t* qT, float* sT, void* stream);
+
+/*
+ * fp8_gemm_blockscaled for power-of-two scales: the same result definition,
+ * but the MFMA applies sA and sB itself as E8M0 operand scales and
+ * accumulates each chunk straight into the FP32 accumulator (no promotion FMA
+ * on the vector ALUs). Every sA and sB value must be a power of two in
+ * [2^-126, 2^127] (the _pow2 quantizers give such scales); only the exponent
+ * field of each value is used. Arguments, layouts and errors as for
+ * fp8_gemm_blockscaled.
+ */
+FP8BS_API int fp8_gemm_blockscaled_pow2(const uint8_t* A, const float* sA, const uint8_t* B,
                          const float* sB, int b_scale_mode, uint16_t* C,
                          int64_t M, int64_t N, int64_t K, void* stream);
 

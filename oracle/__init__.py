@@ -33,7 +33,7 @@ integer matmul), never against this package itself.
 """
 
 from .e4m3 import (E4M3_MAX, e4m3_decode, e4m3_encode, e4m3_finite_values)
-from .quant import (GROUP, bf16_bits_to_f32, group_scale, quant_act_1x128,
+from .quant import (GROUP, bf16_bits_to_f32, group_scale, pow2_scale, quant_act_1x128,
                     quant_act_128x1_T, quant_w_128x128)
 from .gemm import gemm_ref, grouped_gemm_ref, gemm_ref_rows
 from .grouped import grouped_wgrad_ref, padded_group_starts, quant_act_128x1_T_grouped
@@ -42,7 +42,7 @@ from .tolerance import bf16_ulp, check_gemm, bf16_bits_to_f64
 
 __all__ = [
     "E4M3_MAX", "e4m3_decode", "e4m3_encode", "e4m3_finite_values", "GROUP",
-    "bf16_bits_to_f32", "group_scale", "quant_act_1x128", "quant_act_128x1_T",
+    "bf16_bits_to_f32", "group_scale", "pow2_scale", "quant_act_1x128", "quant_act_128x1_T",
     "quant_w_128x128", "gemm_ref", "grouped_gemm_ref", "gemm_ref_rows",
     "bf16_ulp", "check_gemm", "bf16_bits_to_f64", "grouped_wgrad_ref", "padded_group_starts",
     "quant_act_128x1_T_grouped", "check_combine", "combine_ref", "dispatch_quant", "route",

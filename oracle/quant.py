@@ -51,16 +51,35 @@ def group_scale(amax):
     return np.where(s == 0, np.float32(1.0), s).astype(np.float32)
 
 
+def pow2_scale(amax):
+    """Power-of-two variant: the smallest power of two not below group_scale(amax)
+    (fl32(amax / 448), 1.0 for a zero group) and not below 2^-126.
+
+    Reading for the hardware-scaled variant: gfx950's MFMA takes E8M0 (pure
+    power-of-two) operand scales, and the smallest such scale that keeps the
+    group's largest value inside the E4M3 range is the ceiling power of two.
+    """
+    r = group_scale(amax).astype(np.float64)          # exact widening
+    m, e = np.frexp(r)                                # r = m 2^e, m in [0.5, 1)
+    s = np.where(m == 0.5, r, np.ldexp(1.0, e))
+    return np.maximum(s, 2.0 ** -126).astype(np.float32)
+
+
+def _scale(amax, pow2):
+    return pow2_scale(amax) if pow2 else group_scale(amax)
+
+
 def _cast_group(x, s):
     """codes = E4M3(fl32(x / s)) with s broadcast over the group."""
     y = (x / s).astype(np.float32)        # numpy float32 division is IEEE, round-to-nearest-even
     return e4m3_encode(y)
 
 
-def quant_act_1x128(x):
+def quant_act_1x128(x, pow2=False):
     """Activation quantization, one scale per (row m, 128-wide K chunk kb).
 
     x: [M][K] float32 (or BF16 bits). Returns q[M][K] uint8, s[K/128][M] float32.
+    pow2 selects the power-of-two scale (pow2_scale).
     """
     x = _as_f32(x)
     M, K = x.shape
@@ -69,12 +88,12 @@ def quant_act_1x128(x):
     nkb = K // GROUP
     g = x.reshape(M, nkb, GROUP)                      # group (m, kb)
     amax = np.max(np.abs(g), axis=2) if M else np.zeros((0, nkb), np.float32)
-    s = group_scale(amax)                             # [M][nkb]
+    s = _scale(amax, pow2)                            # [M][nkb]
     q = _cast_group(g, s[:, :, None]).reshape(M, K)
     return q, np.ascontiguousarray(s.T)
 
 
-def quant_w_128x128(w, transposed=False):
+def quant_w_128x128(w, transposed=False, pow2=False):
     """Weight quantization, one scale per 128x128 block (nb, kb).
 
     w: [N][K] float32 (or BF16 bits). Returns q[N][K], s[N/128][K/128]; with
@@ -88,14 +107,14 @@ def quant_w_128x128(w, transposed=False):
     nnb, nkb = N // GROUP, K // GROUP
     blk = w.reshape(nnb, GROUP, nkb, GROUP)           # [nb][i][kb][j]
     amax = np.max(np.abs(blk), axis=(1, 3))           # [nb][kb]
-    s = group_scale(amax)
+    s = _scale(amax, pow2)
     q = _cast_group(blk, s[:, None, :, None]).reshape(N, K)
     if not transposed:
         return q, s
     return q, s, np.ascontiguousarray(q.T), np.ascontiguousarray(s.T)
 
 
-def quant_act_128x1_T(x):
+def quant_act_128x1_T(x, pow2=False):
     """Wgrad-operand quantization, one scale per (token chunk tb, channel c).
 
     x: [M][C] float32 (or BF16 bits), M a multiple of 128. Groups are 128
@@ -109,6 +128,6 @@ def quant_act_128x1_T(x):
     ntb = M // GROUP
     g = x.reshape(ntb, GROUP, C)                      # group (tb, c) = g[tb, :, c]
     amax = np.max(np.abs(g), axis=1)                  # [ntb][C]
-    s = group_scale(amax)
+    s = _scale(amax, pow2)
     q = _cast_group(g, s[:, None, :]).reshape(M, C)
     return np.ascontiguousarray(q.T), s
