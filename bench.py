@@ -34,7 +34,7 @@ PEAK_FP8_TFLOPS = 5000.0     # MI355X dense FP8 MFMA (published)
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E (published)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "fp8_block_scaled_x1_amd", "csrc", f)
-                  for f in ("gemm.hip", "quant.hip", "device_common.h")]
+                  for f in ("gemm.hip", "quant.hip", "moe.hip", "device_common.h")]
 
 
 def kernel_source_digest():
