@@ -95,31 +95,26 @@ typedef __attribute__((address_space(3))) void* lds_ptr;
 // rather than the compiler builtin because the compiler cannot tell the two
 // pipeline stages apart and would otherwise wait for the next stage's loads
 // before every read of the current one. The caller waits (s_waitcnt + barrier)
-// before reading what these loads wrote. M0 is saved and restored around the
-// load; the asm has no VGPR outputs.
+// before reading what these loads wrote. M0 is declared clobbered (one
+// scalar move per load instead of a save and a restore); the asm has no VGPR
+// outputs.
 __device__ __forceinline__ void lds_dma16(const void* base, uint32_t voff, uint32_t lds_addr) {
-  uint32_t saved;
   asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %3\n\t"
+      "s_mov_b32 m0, %2\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, %2\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
+      "global_load_lds_dwordx4 %0, %1"
+      :
       : "v"(voff), "s"(base), "s"(lds_addr)
-      : "memory");
+      : "memory", "m0");
 }
 __device__ __forceinline__ void lds_dma4(const void* base, uint32_t voff, uint32_t lds_addr) {
-  uint32_t saved;
   asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %3\n\t"
+      "s_mov_b32 m0, %2\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dword %1, %2\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
+      "global_load_lds_dword %0, %1"
+      :
       : "v"(voff), "s"(base), "s"(lds_addr)
-      : "memory");
+      : "memory", "m0");
 }
 
 __device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
@@ -234,12 +229,18 @@ __device__ __forceinline__ void run_tile(const Tile& t, uint8_t* smem) {
   // Scale vectors: piece q = (7 - wave) mod pieces (64 floats, one 4-byte load
   // per lane) of sA[kb][m0 ..] and, in row mode, of sB[kb][n0 ..]; rows are
   // clamped, lanes past the tile write into the slot's padding, and pieces
-  // loaded by two waves carry the same bytes.
+  // loaded by two waves carry the same bytes. In block mode every wave loads
+  // the chunk's B scales of the tile's (at most kSBlk) 128-column blocks,
+  // sB[n0/128 + l][kb] for lane l (lanes past them repeat the last one), so no
+  // scalar memory load sits in the loop (its return would gate every LDS wait).
   const int qa = (7 - wave) % G::kAPieces, qb = (7 - wave) % G::kBPieces;
   const uint32_t sa_off = 4u * (uint32_t)min(t.m0 + 64 * qa + lane, a_last);
-  const uint32_t sb_off = 4u * (uint32_t)min(t.n0 + 64 * qb + lane, b_last);
+  constexpr int kSBlk = G::BN / BK + 2;
+  const int blk_first = t.n0 / BK;
+  const uint32_t sb_off = ROW_MODE ? 4u * (uint32_t)min(t.n0 + 64 * qb + lane, b_last)
+                                   : 4u * (uint32_t)(min(blk_first + min(lane, kSBlk - 1), b_last / BK) * nkb);
   // loads per wave per chunk of each operand
-  constexpr int kNA = kAL + 1, kNB = kBL + (ROW_MODE ? 1 : 0);
+  constexpr int kNA = kAL + 1, kNB = kBL + 1;
 
   const uint32_t lds = lds_addr_of(smem);
   // j-th load of this wave for operand A (B) of chunk kb into ring slot `slot`
@@ -254,8 +255,10 @@ __device__ __forceinline__ void run_tile(const Tile& t, uint8_t* smem) {
     const uint32_t st = lds + (uint32_t)(G::kBRing + slot * G::kBSlot);
     if (j < kBL)
       lds_dma16(t.B + (int64_t)kb * BK, boffs[j], st + blds[j]);
-    else
+    else if (ROW_MODE)
       lds_dma4(t.sB + (int64_t)kb * t.N, sb_off, st + (uint32_t)(G::BN * BK + 256 * qb));
+    else
+      lds_dma4(t.sB + kb, sb_off, st + (uint32_t)(G::BN * BK));
   };
   auto issue_a = [&](int kb, int slot) {
 #pragma unroll
@@ -281,8 +284,8 @@ __device__ __forceinline__ void run_tile(const Tile& t, uint8_t* smem) {
   const int blk_lo = min(ncol0, b_last) / BK;
   const int blk_hi = min(blk_lo + 1, b_last / BK);
   const int split = min(NS, (BK - (ncol0 & (BK - 1))) / 16);
-  const float* sbb_lo = t.sB + (int64_t)blk_lo * nkb;
-  const float* sbb_hi = t.sB + (int64_t)blk_hi * nkb;
+  // the slot's B-scale area holds the chunk's scales of blocks blk_first ..
+  const int sbi_lo = blk_lo - blk_first, sbi_hi = blk_hi - blk_first;
 
   // The fragments of the smaller operand ("held", NH of them) are read once per
   // chunk; those of the other ("streamed", NT) one step ahead of their use.
@@ -324,12 +327,14 @@ __device__ __forceinline__ void run_tile(const Tile& t, uint8_t* smem) {
   auto read_t = [&](int kb, int t) {
     return read_frag(HA ? slot_b(kb) : slot_a(kb), t_sub + t, lane);
   };
+  // The streamed fragment first, then the held ones in order of use, so that
+  // the chunk's first MFMAs wait only for the reads they need.
   auto read_chunk_start = [&](int kb, v8i (&hf)[NH], v8i& tf, Scales& sc) {
     const uint8_t* As = slot_a(kb);
     const uint8_t* Bs = slot_b(kb);
+    tf = read_t(kb, 0);
 #pragma unroll
     for (int h = 0; h < NH; ++h) hf[h] = read_frag(HA ? As : Bs, h_sub + h, lane);
-    tf = read_t(kb, 0);
     const float* sAs = reinterpret_cast<const float*>(As + G::BM * BK) + wm * WM + (lane & 15);
     const float* sBs = reinterpret_cast<const float*>(Bs + G::BN * BK) + wn * WN + 4 * (lane >> 4);
 #pragma unroll
@@ -341,8 +346,9 @@ __device__ __forceinline__ void run_tile(const Tile& t, uint8_t* smem) {
         sc.sbr[j][0] = v.x; sc.sbr[j][1] = v.y; sc.sbr[j][2] = v.z; sc.sbr[j][3] = v.w;
       }
     } else {
-      sc.lo = sbb_lo[kb];
-      sc.hi = sbb_hi[kb];
+      const float* sBb = reinterpret_cast<const float*>(Bs + G::BN * BK);
+      sc.lo = sBb[sbi_lo];
+      sc.hi = sBb[sbi_hi];
     }
   };
   // promotion of MFMA tile (i, j): scaled FP32 partial into the FP32
@@ -410,6 +416,10 @@ __device__ __forceinline__ void run_tile(const Tile& t, uint8_t* smem) {
   if constexpr (kDeepA) issue_a(min(1, nkb - 1), 1);
   if constexpr (kDeepB) issue_b(min(1, nkb - 1), 1);
   barrier(0);
+  // Retire every scalar load issued so far (kernel arguments), as the
+  // compiler sees it: with one pending, each LDS wait in the loop would have
+  // to drain all LDS reads (lgkmcnt(0)) instead of only those it needs.
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt, expcnt unconstrained
 
   // The main loop, compiled once per block split that can occur.
   auto main_loop = [&](auto split_c) {
@@ -505,7 +515,8 @@ __device__ __forceinline__ void run_tile(const Tile& t, uint8_t* smem) {
 #pragma unroll
       for (int j = 0; j < NS; ++j) eb[j] = (int)(__float_as_uint(sBs[16 * j]) >> 23);
     } else {
-      const int elo = (int)(__float_as_uint(sbb_lo[kb]) >> 23), ehi = (int)(__float_as_uint(sbb_hi[kb]) >> 23);
+      const float* sBb = reinterpret_cast<const float*>(slot_b(kb) + G::BN * BK);
+      const int elo = (int)(__float_as_uint(sBb[sbi_lo]) >> 23), ehi = (int)(__float_as_uint(sBb[sbi_hi]) >> 23);
 #pragma unroll
       for (int j = 0; j < NS; ++j) eb[j] = j < split ? elo : ehi;
     }
@@ -514,9 +525,9 @@ __device__ __forceinline__ void run_tile(const Tile& t, uint8_t* smem) {
     v8i hf[NH];
     v8i tf;
     int ea[MS], eb[NS];
+    tf = read_t(0, 0);
 #pragma unroll
     for (int h = 0; h < NH; ++h) hf[h] = read_frag(HA ? slot_a(0) : slot_b(0), h_sub + h, lane);
-    tf = read_t(0, 0);
     read_scales_hw(0, ea, eb);
     for (int kb = 0; kb < nkb; ++kb) {
 #pragma unroll
@@ -534,9 +545,9 @@ __device__ __forceinline__ void run_tile(const Tile& t, uint8_t* smem) {
       }
       barrier(kb + 1);
       const int kn = min(kb + 1, nkb - 1);
+      tf = read_t(kn, 0);
 #pragma unroll
       for (int h = 0; h < NH; ++h) hf[h] = read_frag(HA ? slot_a(kn) : slot_b(kn), h_sub + h, lane);
-      tf = read_t(kn, 0);
       read_scales_hw(kn, ea, eb);
       __builtin_amdgcn_sched_barrier(0);
     }
