@@ -10,8 +10,9 @@ the 128x1 transposed quantizer), the grouped MoE expert GEMMs and their
 backward (grouped Dgrad, grouped 128x1 transposed quantizers, per-expert
 Wgrad), the MoE dispatch with its FP8 payload and the BF16 combine, the
 decode-shaped grouped GEMM, the Fprop whose GEMM writes the next layer's
-1x128-quantized input directly (fused quantizing epilogue), and the Fprop with
-power-of-two scales applied by the MFMA itself (E8M0 variant).
+1x128-quantized input directly (fused quantizing epilogue; also with the
+transposed 128x1 copy for the backward), and the Fprop with power-of-two
+scales applied by the MFMA itself (E8M0 variant).
 
 Prints one JSON line. `value` is whole-step throughput with inputs resident in
 HBM; `roofline` describes the dominant kernel, timed live with HIP events on
@@ -101,7 +102,7 @@ def setup_dense_fprop(torch, fb, dev, M=4096, N=7168, K=7168, fused=False, pow2=
     and the MFMA applies them (E8M0 operand scales)."""
     import workloads
     sets = []
-    R = _rotations(M * K * 2 + N * K * 2 + M * K + N * K + M * N * (1 if fused else 2))
+    R = _rotations(M * K * 2 + N * K * 2 + M * K + N * K + M * N * (int(fused) if fused else 2))
     for r in range(R):
         d = workloads.dense_fprop(device=dev, seed=r, M=M, N=N, K=K)
         sets.append({
@@ -114,6 +115,9 @@ def setup_dense_fprop(torch, fb, dev, M=4096, N=7168, K=7168, fused=False, pow2=
         if fused:
             sets[-1]["Q"] = torch.empty((M, N), dtype=torch.uint8, device=dev)
             sets[-1]["sQ"] = torch.empty((N // 128, M), dtype=torch.float32, device=dev)
+        if fused == 2:
+            sets[-1]["QT"] = torch.empty((N, M), dtype=torch.uint8, device=dev)
+            sets[-1]["sQT"] = torch.empty((M // 128, N), dtype=torch.float32, device=dev)
         else:
             sets[-1]["C"] = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     L = fb.lib()
@@ -134,6 +138,11 @@ def setup_dense_fprop(torch, fb, dev, M=4096, N=7168, K=7168, fused=False, pow2=
             rc |= L.fp8_gemm_blockscaled_pow2(s["qx"].data_ptr(), s["sx"].data_ptr(), s["qw"].data_ptr(),
                                               s["sw"].data_ptr(), fb.SCALE_BLOCK128, s["C"].data_ptr(), M, N, K,
                                               stream)
+        elif fused == 2:
+            rc |= L.fp8_gemm_blockscaled_q1x128_q128x1T(s["qx"].data_ptr(), s["sx"].data_ptr(), s["qw"].data_ptr(),
+                                                        s["sw"].data_ptr(), fb.SCALE_BLOCK128, s["Q"].data_ptr(),
+                                                        s["sQ"].data_ptr(), s["QT"].data_ptr(), s["sQT"].data_ptr(),
+                                                        M, N, K, stream)
         elif fused:
             rc |= L.fp8_gemm_blockscaled_q1x128(s["qx"].data_ptr(), s["sx"].data_ptr(), s["qw"].data_ptr(),
                                                 s["sw"].data_ptr(), fb.SCALE_BLOCK128, s["Q"].data_ptr(),
@@ -146,9 +155,12 @@ def setup_dense_fprop(torch, fb, dev, M=4096, N=7168, K=7168, fused=False, pow2=
             raise RuntimeError(f"libfp8bs call failed ({rc})")
 
     flops = 2.0 * M * N * K
-    gemm = "gemm_blockscaled_q1x128" if fused else ("gemm_blockscaled_pow2" if pow2 else "gemm_blockscaled")
-    out = (f"Q[{M}x{N}] fp8 + sQ[{N // 128}x{M}] (fused 1x128 quantizing epilogue)" if fused
-           else f"C[{M}x{N}] bf16" + (", power-of-two scales applied by the MFMA (E8M0)" if pow2 else ""))
+    gemm = {0: "gemm_blockscaled_pow2" if pow2 else "gemm_blockscaled", 1: "gemm_blockscaled_q1x128",
+            2: "gemm_blockscaled_q1x128_q128x1T"}[int(fused)]
+    out = {0: f"C[{M}x{N}] bf16" + (", power-of-two scales applied by the MFMA (E8M0)" if pow2 else ""),
+           1: f"Q[{M}x{N}] fp8 + sQ[{N // 128}x{M}] (fused 1x128 quantizing epilogue)",
+           2: f"Q[{M}x{N}] + sQ and QT[{N}x{M}] + sQT (fused 1x128 and transposed 128x1 quantizing epilogue)"
+           }[int(fused)]
     info = {
         "names": ["quant_act_1x128", "quant_w_128x128", gemm],
         "step_flops": flops,
@@ -166,6 +178,10 @@ def setup_dense_fprop(torch, fb, dev, M=4096, N=7168, K=7168, fused=False, pow2=
 
 def setup_fprop_q1x128(torch, fb, dev):
     return setup_dense_fprop(torch, fb, dev, fused=True)
+
+
+def setup_fprop_qboth(torch, fb, dev):
+    return setup_dense_fprop(torch, fb, dev, fused=2)
 
 
 def setup_fprop_pow2(torch, fb, dev):
@@ -486,7 +502,7 @@ def setup_copy(torch, fb, dev, nbytes=None):
 
 
 WORKLOADS = {"copy": setup_copy, "dense_fprop": setup_dense_fprop, "fprop_q1x128": setup_fprop_q1x128,
-             "fprop_pow2": setup_fprop_pow2,
+             "fprop_pow2": setup_fprop_pow2, "fprop_qboth": setup_fprop_qboth,
              "backward": setup_backward, "moe": setup_moe, "moe_backward": setup_moe_backward,
              "moe_dispatch": setup_moe_dispatch, "decode": setup_decode}
 

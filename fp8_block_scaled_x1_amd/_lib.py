@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libfp8bs.so")
 
 F32, BF16 = 0, 1
 SCALE_BLOCK128, SCALE_ROW = 0, 1
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 _c_int64 = ctypes.c_int64
 _vp = ctypes.c_void_p
@@ -33,6 +33,8 @@ _SIGNATURES = {
     "fp8_gemm_blockscaled_pow2": [_vp, _vp, _vp, _vp, ctypes.c_int, _vp, _c_int64, _c_int64, _c_int64, _vp],
     "fp8_gemm_blockscaled_q1x128": [_vp, _vp, _vp, _vp, ctypes.c_int, _vp, _vp, _c_int64, _c_int64,
                                     _c_int64, _vp],
+    "fp8_gemm_blockscaled_q1x128_q128x1T": [_vp, _vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp, _vp, _c_int64,
+                                            _c_int64, _c_int64, _vp],
     "fp8_grouped_gemm_blockscaled": [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _c_int64, _c_int64,
                                      _c_int64, _vp],
     "fp8_quant_act_128x1_T_grouped": [_vp, ctypes.c_int, _c_int64, _c_int64, _vp, ctypes.c_int, _c_int64, _vp,
@@ -193,6 +195,22 @@ def fp8_gemm_blockscaled_q1x128(A, sA, B, sB, b_scale_mode=SCALE_BLOCK128):
            lib().fp8_gemm_blockscaled_q1x128(pa, psa, pb, psb, int(b_scale_mode), Q.data_ptr(),
                                              sQ.data_ptr(), M, N, K, _stream(A)))
     return Q, sQ
+
+
+def fp8_gemm_blockscaled_q1x128_q128x1T(A, sA, B, sB, b_scale_mode=SCALE_BLOCK128):
+    """The GEMM's BF16 result quantized both ways: (Q [M][N], sQ [N/128][M]) 1x128 and
+    (QT [N][M], sQT [M/128][N]) 128x1 transposed; M a multiple of 128."""
+    M, N, K, (pa, psa, pb, psb) = _gemm_operands(A, sA, B, sB, b_scale_mode)
+    dev = A.device
+    Q = torch.empty((M, N), dtype=torch.uint8, device=dev)
+    sQ = torch.empty((N // 128, M), dtype=torch.float32, device=dev)
+    QT = torch.empty((N, M), dtype=torch.uint8, device=dev)
+    sQT = torch.empty((M // 128, N), dtype=torch.float32, device=dev)
+    _check("fp8_gemm_blockscaled_q1x128_q128x1T",
+           lib().fp8_gemm_blockscaled_q1x128_q128x1T(pa, psa, pb, psb, int(b_scale_mode), Q.data_ptr(),
+                                                     sQ.data_ptr(), QT.data_ptr(), sQT.data_ptr(), M, N, K,
+                                                     _stream(A)))
+    return Q, sQ, QT, sQT
 
 
 def fp8_grouped_gemm_blockscaled(A, sA, B, sB, group_offsets, out=None):

@@ -153,6 +153,22 @@ int fp8_gemm_blockscaled_q1x128(const uint8_t* A, const float* sA, const uint8_t
                                                          as_stream(stream)));
 }
 
+int fp8_gemm_blockscaled_q1x128_q128x1T(const uint8_t* A, const float* sA, const uint8_t* B,
+                                        const float* sB, int b_scale_mode, uint8_t* Q, float* sQ,
+                                        uint8_t* QT, float* sQT, int64_t M, int64_t N, int64_t K,
+                                        void* stream) {
+  if (b_scale_mode != FP8BS_SCALE_BLOCK128 && b_scale_mode != FP8BS_SCALE_ROW) return FP8BS_ERR_MODE;
+  if (M < 0 || N < 0 || K <= 0 || K % kG || N % kG || M % kG) return FP8BS_ERR_SHAPE;
+  if (M * K >= kI32 || N * K >= kI32 || M * N >= kI32) return FP8BS_ERR_TOO_LARGE;
+  if (M == 0 || N == 0) return FP8BS_OK;
+  if (!A || !sA || !B || !sB || !Q || !sQ || !QT || !sQT) return FP8BS_ERR_NULL_PTR;
+  if (misaligned(A) || misaligned(sA) || misaligned(B) || misaligned(sB) || misaligned(Q) ||
+      misaligned(sQ) || misaligned(QT) || misaligned(sQT))
+    return FP8BS_ERR_ALIGN;
+  return status_of(fp8bs::launch_gemm_blockscaled_q1x128_q128x1T(A, sA, B, sB, b_scale_mode, Q, sQ, QT, sQT,
+                                                                 M, N, K, as_stream(stream)));
+}
+
 int fp8_grouped_gemm_blockscaled(const uint8_t* A, const float* sA, const uint8_t* B,
                                  const float* sB, uint16_t* C, const int32_t* group_offsets, int E,
                                  int64_t M_total, int64_t N, int64_t K, void* stream) {

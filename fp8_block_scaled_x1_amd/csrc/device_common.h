@@ -176,6 +176,26 @@ __device__ __forceinline__ uint32_t e4m3_div_pack4_bf16(float x0, float x1, floa
   return e4m3_pack4(x0 / g.s, x1 / g.s, x2 / g.s, x3 / g.s);
 }
 
+// Codes of x[r] / g[r].s for four values with four different scales (BF16
+// numbers as inputs), packed little-endian: each quotient as in
+// e4m3_div_pack4_bf16 (one FMA correction where that scale allows it, else the
+// IEEE division), then the clamp and the converter of e4m3_pack4 (the clamp
+// leaves every correction-path quotient's code unchanged: those stay below
+// 464, where the converter already saturates to 448).
+__device__ __forceinline__ uint32_t e4m3_div_cols4_bf16(const float x[4], const GroupDiv g[4]) {
+  float q[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    if (g[r].fast) {
+      const float q0 = x[r] * g[r].r;
+      q[r] = __builtin_copysignf(fmaf(fmaf(-q0, g[r].s, x[r]), g[r].r, q0), x[r]);
+    } else {
+      q[r] = x[r] / g[r].s;
+    }
+  }
+  return e4m3_pack4(q[0], q[1], q[2], q[3]);
+}
+
 // The quotient codes for the input type: checked for F32, one-correction for BF16.
 template <bool BF16>
 __device__ __forceinline__ uint32_t e4m3_div_pack4_t(float x0, float x1, float x2, float x3, const GroupDiv& g) {

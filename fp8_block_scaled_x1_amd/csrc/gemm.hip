@@ -166,6 +166,8 @@ struct Tile {
   uint16_t* C;        // [rows][N] (BF16 output)
   uint8_t* Q;         // [rows][N] (quantized output: E4M3 codes)
   float* sQ;          // [N/128][rows] (quantized output: 1x128 group scales)
+  uint8_t* QT;        // [N][rows] (quantized output, 128x1 groups, transposed codes)
+  float* sQT;         // [rows/128][N] (its scales)
   int m0, row_end;    // tile rows m0 .. m0+BM-1, valid below row_end
   int n0, N, K;       // K: inner length of this tile's product (a multiple of 128)
   int ld;             // row stride of A and B in bytes (K for a plain GEMM)
@@ -181,7 +183,8 @@ __device__ __forceinline__ void wait_and_barrier() {
 }
 // QOUT: the epilogue writes the 1x128 quantization (E4M3 codes and FP32
 // scales per row and 128 columns) of the BF16-rounded result instead of the
-// BF16 result itself.
+// BF16 result itself; QOUT == 2 also writes its 128x1 quantization (128 rows
+// of one column per group), transposed.
 // HW: the scales are powers of two and the MFMA applies them itself, as E8M0
 // block scales of its operands (the exponent field of an FP32 power of two is
 // its E8M0 code); each MFMA then accumulates straight into the FP32
@@ -650,6 +653,53 @@ __device__ __forceinline__ void run_tile(const Tile& t, uint8_t* smem) {
         if (lane < 16 && wn % kGW == 0) t.sQ[(int64_t)grp * t.row_end + m] = g.s;
       }
     }
+    if constexpr (QOUT == 2) {
+      // 128x1 groups: a wave's WM = 128 rows are one group of each of its
+      // columns. Column amax: over the lane's MS rows, then over the 16 lanes
+      // that share the column (xor 1, 2, 4, 8). Each lane encodes its four
+      // columns of row 16i + lane%16 into one word; a 4x4 byte transpose
+      // inside each quad of lanes (DPP quad broadcasts) turns that into four
+      // consecutive rows of one column, one 4-byte piece of a QT row.
+      static_assert(WM == kGroup, "a wave's rows must form one 128-row group");
+      const int m_grp0 = t.m0 + wm * WM;
+      const bool rows_ok = m_grp0 < t.row_end;      // rows % 128 == 0: a group is wholly in or out
+      const int q = lane & 3;
+#pragma unroll
+      for (int j = 0; j < NS; ++j) {
+        GroupDiv gc[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float a = 0.0f;
+#pragma unroll
+          for (int i = 0; i < MS; ++i) a = fmaxf(a, fabsf(v[i][j][r]));
+          a = fmaxf(a, __shfl_xor(a, 1, 64));
+          a = fmaxf(a, __shfl_xor(a, 2, 64));
+          a = fmaxf(a, __shfl_xor(a, 4, 64));
+          a = fmaxf(a, __shfl_xor(a, 8, 64));
+          gc[r] = group_div<true>(a);
+        }
+        const int n_col = n_lane + 16 * j + q;        // this lane's column after the transpose
+        if (rows_ok && group_ok) {
+          if ((lane & 15) == 0)
+            *reinterpret_cast<float4*>(t.sQT + (int64_t)(m_grp0 / kGroup) * t.N + n_lane + 16 * j) =
+                make_float4(gc[0].s, gc[1].s, gc[2].s, gc[3].s);
+#pragma unroll
+          for (int i = 0; i < MS; ++i) {
+            const int w = (int)e4m3_div_cols4_bf16(v[i][j], gc);
+            // quad lane qq's word, broadcast in its quad (quad_perm [qq,qq,qq,qq])
+            const uint32_t w0 = (uint32_t)__builtin_amdgcn_mov_dpp(w, 0x00, 0xF, 0xF, false);
+            const uint32_t w1 = (uint32_t)__builtin_amdgcn_mov_dpp(w, 0x55, 0xF, 0xF, false);
+            const uint32_t w2 = (uint32_t)__builtin_amdgcn_mov_dpp(w, 0xAA, 0xF, 0xF, false);
+            const uint32_t w3 = (uint32_t)__builtin_amdgcn_mov_dpp(w, 0xFF, 0xF, 0xF, false);
+            const uint32_t sh = 8u * (uint32_t)q;
+            const uint32_t out = ((w0 >> sh) & 0xFFu) | (((w1 >> sh) & 0xFFu) << 8) |
+                                 (((w2 >> sh) & 0xFFu) << 16) | (((w3 >> sh) & 0xFFu) << 24);
+            const int m = m_grp0 + 16 * i + (lane & 12);
+            *reinterpret_cast<uint32_t*>(t.QT + (int64_t)n_col * t.row_end + m) = out;
+          }
+        }
+      }
+    }
   }
 }
 
@@ -660,7 +710,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const uint8_t* __rest
                                                             const float* __restrict__ sB,
                                                             uint16_t* __restrict__ C,
                                                             uint8_t* __restrict__ Q,
-                                                            float* __restrict__ sQ, int M, int N,
+                                                            float* __restrict__ sQ,
+                                                            uint8_t* __restrict__ QT,
+                                                            float* __restrict__ sQT, int M, int N,
                                                             int K) {
   __shared__ __align__(16) uint8_t smem[G::kLdsBytes];
   const int tiles_m = (M + G::BM - 1) / G::BM, tiles_n = (N + G::BN - 1) / G::BN;
@@ -669,7 +721,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const uint8_t* __rest
   tile_coords(pid, tiles_m, tiles_n, tm, tn);
   Tile t;
   t.A = A; t.sA = sA; t.sa_stride = M;
-  t.B = B; t.sB = sB; t.C = C; t.Q = Q; t.sQ = sQ;
+  t.B = B; t.sB = sB; t.C = C; t.Q = Q; t.sQ = sQ; t.QT = QT; t.sQT = sQT;
   t.m0 = tm * G::BM; t.row_end = M;
   t.n0 = tn * G::BN; t.N = N; t.K = K; t.ld = K;
   run_tile<G, ROW_MODE, QOUT, HW>(t, smem);
@@ -697,7 +749,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
   t.A = A; t.sA = sA; t.sa_stride = M_total;
   t.B = B + (int64_t)e_found * N * K;
   t.sB = sB + (int64_t)e_found * (N / BK) * nkb;
-  t.C = C; t.Q = nullptr; t.sQ = nullptr;
+  t.C = C; t.Q = nullptr; t.sQ = nullptr; t.QT = nullptr; t.sQT = nullptr;
   t.m0 = r0 + tm * G::BM; t.row_end = r1;
   t.n0 = tn * G::BN; t.N = N; t.K = K; t.ld = K;
   run_tile<G, 0>(t, smem);
@@ -746,7 +798,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_wgrad_kernel(
   Tile t;
   t.A = A + (int64_t)es.base * BK; t.sA = sA + (int64_t)es.base * N; t.sa_stride = N;
   t.B = B + (int64_t)es.base * BK; t.sB = sB + (int64_t)es.base * K;
-  t.C = Ce; t.Q = nullptr; t.sQ = nullptr;
+  t.C = Ce; t.Q = nullptr; t.sQ = nullptr; t.QT = nullptr; t.sQT = nullptr;
   t.m0 = tm * G::BM; t.row_end = N;
   t.n0 = tn * G::BN; t.N = K; t.K = groups * BK; t.ld = ld;
   run_tile<G, 1>(t, smem);
@@ -786,14 +838,14 @@ int pick_dense(int64_t M, int64_t N) {
 template <class G, int QOUT, int HW = 0>
 hipError_t launch_dense(const uint8_t* A, const float* sA, const uint8_t* B, const float* sB,
                         int row_mode, uint16_t* C, uint8_t* Q, float* sQ, int64_t M, int64_t N,
-                        int64_t K, hipStream_t stream) {
+                        int64_t K, hipStream_t stream, uint8_t* QT = nullptr, float* sQT = nullptr) {
   const int tiles = (int)(((M + G::BM - 1) / G::BM) * ((N + G::BN - 1) / G::BN));
   if (row_mode)
     hipLaunchKernelGGL((gemm_kernel<G, 1, QOUT, HW>), dim3(tiles), dim3(kThreads), 0, stream, A, sA, B, sB,
-                       C, Q, sQ, (int)M, (int)N, (int)K);
+                       C, Q, sQ, QT, sQT, (int)M, (int)N, (int)K);
   else
     hipLaunchKernelGGL((gemm_kernel<G, 0, QOUT, HW>), dim3(tiles), dim3(kThreads), 0, stream, A, sA, B, sB,
-                       C, Q, sQ, (int)M, (int)N, (int)K);
+                       C, Q, sQ, QT, sQT, (int)M, (int)N, (int)K);
   return hipGetLastError();
 }
 
@@ -832,6 +884,15 @@ hipError_t launch_gemm_blockscaled_q1x128(const uint8_t* A, const float* sA, con
   const int64_t c2 = round_cost<Cfg224x256>(((M + 223) / 224) * tn, cus);
   if (c2 < c0) return launch_dense<Cfg224x256, 1>(A, sA, B, sB, row_mode, nullptr, Q, sQ, M, N, K, stream);
   return launch_dense<Cfg256x256, 1>(A, sA, B, sB, row_mode, nullptr, Q, sQ, M, N, K, stream);
+}
+
+hipError_t launch_gemm_blockscaled_q1x128_q128x1T(const uint8_t* A, const float* sA, const uint8_t* B,
+                                                  const float* sB, int row_mode, uint8_t* Q, float* sQ,
+                                                  uint8_t* QT, float* sQT, int64_t M, int64_t N, int64_t K,
+                                                  hipStream_t stream) {
+  using namespace gemm;
+  // 256x256 tiles: each wave's 128 rows form one 128x1 group
+  return launch_dense<Cfg256x256, 2>(A, sA, B, sB, row_mode, nullptr, Q, sQ, M, N, K, stream, QT, sQT);
 }
 
 hipError_t launch_grouped_gemm_blockscaled(const uint8_t* A, const float* sA, const uint8_t* B,

@@ -31,6 +31,10 @@ hipError_t launch_grouped_gemm_wgrad(const uint8_t* A, const float* sA, const ui
 hipError_t launch_quant_act_128x1_T_grouped(const void* x, bool bf16, int64_t M_total, int64_t C,
                                             const int32_t* offsets, int E, int64_t ld, uint8_t* qT,
                                             float* sT, hipStream_t stream);
+hipError_t launch_gemm_blockscaled_q1x128_q128x1T(const uint8_t* A, const float* sA, const uint8_t* B,
+                                                  const float* sB, int row_mode, uint8_t* Q, float* sQ,
+                                                  uint8_t* QT, float* sQT, int64_t M, int64_t N, int64_t K,
+                                                  hipStream_t stream);
 hipError_t launch_grouped_gemm_blockscaled(const uint8_t* A, const float* sA, const uint8_t* B,
                                            const float* sB, uint16_t* C, const int32_t* offsets,
                                            int E, int64_t M_total, int64_t N, int64_t K,

@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define FP8BS_ABI_VERSION 5
+#define FP8BS_ABI_VERSION 6
 
 #ifndef FP8BS_API
 #define FP8BS_API __attribute__((visibility("default")))
@@ -176,6 +176,24 @@ FP8BS_API int fp8_gemm_blockscaled_pow2(const uint8_t* A, const float* sA, const
 FP8BS_API int fp8_gemm_blockscaled_q1x128(const uint8_t* A, const float* sA, const uint8_t* B,
                          const float* sB, int b_scale_mode, uint8_t* Q, float* sQ,
                          int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
+ * The quantizing epilogue with both layouts the next layer needs: the 1x128
+ * quantization (Q, sQ, as fp8_gemm_blockscaled_q1x128 writes it) and the
+ * 128x1 quantization written transposed (QT, sQT: exactly what
+ * fp8_quant_act_128x1_T, BF16 input, gives for the same BF16 result), the
+ * copy the next layer's Wgrad GEMM reads (report sections 3.3.1-3.3.2: the
+ * FP8 Wgrad GEMM lets activations be cached in FP8 for the backward pass,
+ * innerforce.co.kr page).
+ *   Q   [M][N] uint8,  sQ  [N/128][M] float32
+ *   QT  [N][M] uint8,  sQT [M/128][N] float32
+ * M must be a multiple of 128 (whole 128-row groups); otherwise as for
+ * fp8_gemm_blockscaled_q1x128.
+ */
+FP8BS_API int fp8_gemm_blockscaled_q1x128_q128x1T(const uint8_t* A, const float* sA, const uint8_t* B,
+                         const float* sB, int b_scale_mode, uint8_t* Q, float* sQ,
+                         uint8_t* QT, float* sQT, int64_t M, int64_t N, int64_t K,
+                         void* stream);
 
 /*
  * Grouped (per-expert) form for MoE experts (report sections 3.3.2 and

@@ -33,6 +33,7 @@ def test_header_declares_the_entry_points():
     names = set(_declared_functions())
     assert {"fp8_quant_act_1x128", "fp8_quant_w_128x128", "fp8_quant_act_128x1_T",
             "fp8_quant_act_128x1_T_grouped", "fp8_gemm_blockscaled", "fp8_gemm_blockscaled_q1x128",
+            "fp8_gemm_blockscaled_q1x128_q128x1T",
             "fp8_grouped_gemm_blockscaled", "fp8_grouped_gemm_wgrad", "fp8_moe_dispatch",
             "fp8_moe_dispatch_workspace_bytes", "fp8_moe_combine", "fp8_quant_act_1x128_pow2",
             "fp8_quant_w_128x128_pow2", "fp8_quant_act_128x1_T_pow2", "fp8_gemm_blockscaled_pow2",
@@ -46,7 +47,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.fp8bs_abi_version() == fb.ABI_VERSION == 5
+    assert L.fp8bs_abi_version() == fb.ABI_VERSION == 6
     for code in range(-7, 1):
         assert fb.status_string(code) not in ("", "unknown status")
     assert fb.status_string(-99) == "unknown status"

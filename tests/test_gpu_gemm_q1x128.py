@@ -1,10 +1,12 @@
-"""GPU parity of the GEMM with the fused 1x128 quantizing epilogue.
+"""GPU parity of the GEMM with the fused quantizing epilogues.
 
 fp8_gemm_blockscaled_q1x128 must write exactly the oracle's 1x128
 quantization (codes and scales, bit for bit) of the BF16 result that
-fp8_gemm_blockscaled writes for the same operands; that BF16 result is held
-to the oracle GEMM's acceptance bound here as well, so the pair pins the fused
-output to the oracle without any GPU quantizer in between.
+fp8_gemm_blockscaled writes for the same operands, and
+fp8_gemm_blockscaled_q1x128_q128x1T also the oracle's transposed 128x1
+quantization of it; that BF16 result is held to the oracle GEMM's acceptance
+bound here as well, so each pair pins the fused output to the oracle without
+any GPU quantizer in between.
 """
 
 import numpy as np
@@ -146,3 +148,72 @@ def test_fused_q1x128_rejects_bad_arguments(dev):
     assert L.fp8_gemm_blockscaled_q1x128(*p, 0, Q.data_ptr() + 1, sQ.data_ptr(), 128, 128, 128,
                                          None) != 0
     assert L.fp8_gemm_blockscaled_q1x128(*p, 0, Q.data_ptr(), sQ.data_ptr(), 128, 128, 128, None) == 0
+
+
+# ---------------------------------------------------------------------------
+# both layouts: 1x128 and the transposed 128x1 copy (M a multiple of 128)
+# ---------------------------------------------------------------------------
+
+def _both_vs_oracle(dev, A, sA, B, sB, mode, what):
+    args = (A.to(dev), sA.to(dev), B.to(dev), sB.to(dev), mode)
+    C = fb.fp8_gemm_blockscaled(*args)
+    Q, sQ, QT, sQT = fb.fp8_gemm_blockscaled_q1x128_q128x1T(*args)
+    torch.cuda.synchronize()
+    M, N = C.shape
+    assert QT.shape == (N, M) and sQT.shape == (M // 128, N)
+    ref, absref = oracle.gemm_ref(A.numpy(), sA.numpy(), B.numpy(), sB.numpy(), mode)
+    ok, worst = oracle.check_gemm(bf16_bits(C), ref, absref)
+    assert ok.all(), f"{what}: BF16 result outside the bound (worst {worst:.3g})"
+    qo, so = oracle.quant_act_1x128(bf16_bits(C))
+    assert_codes_equal(u8(Q), qo, f"{what}: 1x128 codes")
+    assert_scales_equal(sQ.cpu().numpy(), so, f"{what}: 1x128 scales")
+    qto, sto = oracle.quant_act_128x1_T(bf16_bits(C))
+    assert_codes_equal(u8(QT), qto, f"{what}: 128x1 transposed codes")
+    assert_scales_equal(sQT.cpu().numpy(), sto, f"{what}: 128x1 scales")
+
+
+@pytest.mark.parametrize("M,N,K", [(128, 128, 128), (256, 256, 384), (384, 640, 256), (1024, 1280, 512),
+                                   (640, 384, 1024)])
+@pytest.mark.parametrize("mode", [MODE_BLOCK, MODE_ROW])
+def test_fused_both_layouts_random_codes(dev, M, N, K, mode):
+    A, B = _codes((M, K), 5 * M + N + K), _codes((N, K), 17 + M + 2 * N + K)
+    sA = _scales((K // 128, M), 3 + M)
+    sB = _scales(_sb_shape(mode, N, K), 11 + N)
+    _both_vs_oracle(dev, A, sA, B, sB, mode, f"both layouts {M}x{N}x{K} mode {mode}")
+
+
+def test_fused_both_layouts_zero_and_wide(dev):
+    M, N, K = 384, 512, 256
+    A, B = _codes((M, K), 31), _codes((N, K), 32)
+    A[128:256] = 0                        # a zero 128-row group for every column
+    B[200] = 0                            # one zero column
+    g = torch.Generator().manual_seed(33)
+    sA = torch.pow(2.0, torch.randint(-30, 31, (K // 128, M), generator=g).float())
+    sB = torch.pow(2.0, torch.randint(-10, 11, (N // 128, K // 128), generator=g).float())
+    _both_vs_oracle(dev, A, sA, B, sB, MODE_BLOCK, "both layouts, zero groups and wide scales")
+
+
+def test_fused_both_layouts_dense_fprop(dev):
+    d = workloads.dense_fprop(device=dev)
+    qx, sx = fb.fp8_quant_act_1x128(d["X"])
+    qw, sw = fb.fp8_quant_w_128x128(d["W"])
+    C = fb.fp8_gemm_blockscaled(qx, sx, qw, sw)
+    Q, sQ, QT, sQT = fb.fp8_gemm_blockscaled_q1x128_q128x1T(qx, sx, qw, sw)
+    q2, s2 = fb.fp8_quant_act_1x128(C)
+    qt2, st2 = fb.fp8_quant_act_128x1_T(C)
+    torch.cuda.synchronize()
+    assert torch.equal(Q, q2) and torch.equal(sQ.view(torch.int32), s2.view(torch.int32))
+    assert torch.equal(QT, qt2) and torch.equal(sQT.view(torch.int32), st2.view(torch.int32))
+    # and one 128-row group of columns against the oracle directly
+    qto, sto = oracle.quant_act_128x1_T(bf16_bits(C[256:384]))
+    assert_codes_equal(u8(QT[:, 256:384]), qto, "dense fprop 128x1 codes, rows 256..383")
+    assert_scales_equal(sQT[2:3].cpu().numpy(), sto, "dense fprop 128x1 scales, rows 256..383")
+
+
+def test_fused_both_layouts_rejects_ragged_m(dev):
+    A = torch.zeros((100, 128), dtype=torch.uint8, device=dev)
+    sA = torch.ones((1, 100), device=dev)
+    B = torch.zeros((128, 128), dtype=torch.uint8, device=dev)
+    sB = torch.ones((1, 1), device=dev)
+    with pytest.raises(fb.Fp8bsError):
+        fb.fp8_gemm_blockscaled_q1x128_q128x1T(A, sA, B, sB)
