@@ -15,7 +15,8 @@
 // registers the MFMA just wrote; the hardware co-issues it with the MFMAs of
 // the next subtile.
 //
-// Structure (one BM x BN output tile per workgroup of 8 waves):
+// Structure (one BM x BN output tile per workgroup of 8 waves; 4 for the
+// hardware-scaled variant's 256x256 tiles):
 //   * one pipeline stage = one K chunk: A[BM][128] + B[BN][128] bytes plus the
 //     chunk's scale vectors, moved L2 -> LDS with direct-to-LDS loads (no VGPR
 //     staging); two stages; one barrier per chunk;
@@ -53,7 +54,6 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 namespace gemm {
 
 constexpr int BK = kGroup;
-constexpr int kThreads = 512;        // 8 waves
 constexpr int kGroupM = 8;           // tile-order grouping for L2 reuse
 constexpr int kXcds = 8;
 
@@ -70,9 +70,11 @@ struct Cfg {
   static constexpr int kBRing = DA * kASlot;                  // B ring follows the A ring
   static constexpr int kLdsBytes = DA * kASlot + DB * kBSlot;
   static constexpr int kASlices = BM / 8, kBSlices = BN / 8;  // 1 KB load slices per chunk
-  static constexpr int kASlicesPerWave = (kASlices + 7) / 8, kBSlicesPerWave = (kBSlices + 7) / 8;
+  static constexpr int kWaves = WGM * WGN, kThreads = 64 * kWaves;
+  static constexpr int kASlicesPerWave = (kASlices + kWaves - 1) / kWaves;
+  static constexpr int kBSlicesPerWave = (kBSlices + kWaves - 1) / kWaves;
   static constexpr bool kHoldB = NS <= MS;                    // hold the smaller operand
-  static_assert(WGM * WGN == 8, "8 waves");
+  static_assert(WGM * WGN == 8 || WGM * WGN == 4, "8 or 4 waves");
   static_assert(WM % 16 == 0 && WN % 16 == 0 && BM % 8 == 0 && BN % 8 == 0, "tile shape");
   static_assert(DA >= 2 && DA <= 3 && DB >= 2 && DB <= 3, "rings two or three deep");
   static_assert(kAPieces <= 4 && kBPieces <= 4, "scale loads");
@@ -87,6 +89,10 @@ using Cfg224x256 = Cfg<224, 256, 2, 4, 2, 3>;
 // 128x256, waves 2x4 of 64x64, both operands three deep: grouped GEMMs with
 // few rows per group (decode), where B is the operand streamed from HBM
 using Cfg128x256d = Cfg<128, 256, 2, 4, 3, 3>;
+// 256x256 with 4 waves of 128x128 (one per SIMD, up to 512 registers each):
+// only for the hardware-scaled variant, whose accumulators the MFMA updates
+// in place (they can live in AGPRs), so no promotion needs them in VGPRs
+using Cfg256x256w4 = Cfg<256, 256, 2, 2, 2, 2>;
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
@@ -196,20 +202,21 @@ __device__ __forceinline__ void run_tile(const Tile& t, uint8_t* smem) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  __builtin_assume(wave >= 0 && wave < 8);
+  constexpr int kW = G::kWaves;
+  __builtin_assume(wave >= 0 && wave < kW);
   const int wm = wave / G::WGN, wn = wave % G::WGN;
   const int nkb = t.K / BK;
   const int a_last = t.row_end - 1;
   const int b_last = t.N - 1;
 
   // Direct-to-LDS operand loads. Slice s (1 KB) of an operand covers its tile
-  // rows 8s .. 8s+7; this wave loads slices wave, wave+8, ... Lane p fetches
+  // rows 8s .. 8s+7; this wave loads slices wave, wave+W, ... (W waves). Lane p fetches
   // row 8s + p/8, logical 16-byte column (p%8) ^ swz(row), and writes physical
   // column p%8. Offsets are 32-bit from a uniform base (M*K, N*K < 2^31); rows
   // past the end are clamped (their results are never stored). A wave whose
   // last slice index is past the tile repeats its previous slice (same bytes
   // to the same place), so every wave issues the same number of loads.
-  auto slice_of = [&](int j, int slices) { return wave + 8 * j < slices ? wave + 8 * j : wave + 8 * (j - 1); };
+  auto slice_of = [&](int j, int slices) { return wave + kW * j < slices ? wave + kW * j : wave + kW * (j - 1); };
   auto slice_off = [&](int s, int first, int last) {
     const int rr = s * 8 + (lane >> 3);
     const uint32_t col = (uint32_t)(((lane & 7) ^ swz(rr)) << 4);
@@ -229,14 +236,14 @@ __device__ __forceinline__ void run_tile(const Tile& t, uint8_t* smem) {
     boffs[j] = slice_off(sl, t.n0, b_last);
     blds[j] = (uint32_t)sl * 1024u;
   }
-  // Scale vectors: piece q = (7 - wave) mod pieces (64 floats, one 4-byte load
+  // Scale vectors: piece q = (waves - 1 - wave) mod pieces (64 floats, one 4-byte load
   // per lane) of sA[kb][m0 ..] and, in row mode, of sB[kb][n0 ..]; rows are
   // clamped, lanes past the tile write into the slot's padding, and pieces
   // loaded by two waves carry the same bytes. In block mode every wave loads
   // the chunk's B scales of the tile's (at most kSBlk) 128-column blocks,
   // sB[n0/128 + l][kb] for lane l (lanes past them repeat the last one), so no
   // scalar memory load sits in the loop (its return would gate every LDS wait).
-  const int qa = (7 - wave) % G::kAPieces, qb = (7 - wave) % G::kBPieces;
+  const int qa = (kW - 1 - wave) % G::kAPieces, qb = (kW - 1 - wave) % G::kBPieces;
   const uint32_t sa_off = 4u * (uint32_t)min(t.m0 + 64 * qa + lane, a_last);
   constexpr int kSBlk = G::BN / BK + 2;
   const int blk_first = t.n0 / BK;
@@ -704,7 +711,7 @@ __device__ __forceinline__ void run_tile(const Tile& t, uint8_t* smem) {
 }
 
 template <class G, int ROW_MODE, int QOUT, int HW = 0>
-__global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const uint8_t* __restrict__ A,
+__global__ __launch_bounds__(G::kThreads, 1) void gemm_kernel(const uint8_t* __restrict__ A,
                                                             const float* __restrict__ sA,
                                                             const uint8_t* __restrict__ B,
                                                             const float* __restrict__ sB,
@@ -731,7 +738,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const uint8_t* __rest
 // ceil(rows/BM) x ceil(N/BN), numbered expert-major. The grid is an upper
 // bound on the total; workgroups past the last tile exit at once.
 template <class G>
-__global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
+__global__ __launch_bounds__(G::kThreads, 1) void grouped_gemm_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ sA, const uint8_t* __restrict__ B,
     const float* __restrict__ sB, uint16_t* __restrict__ C, const int32_t* __restrict__ offsets,
     int E, int M_total, int N, int K) {
@@ -769,7 +776,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
 // of each expert in turn (in the grouped tile order that run is a compact
 // block of m- and n-tiles, whose operand panels stay in that XCD's L2).
 template <class G>
-__global__ __launch_bounds__(kThreads, 1) void grouped_wgrad_kernel(
+__global__ __launch_bounds__(G::kThreads, 1) void grouped_wgrad_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ sA, const uint8_t* __restrict__ B,
     const float* __restrict__ sB, uint16_t* __restrict__ C, const int32_t* __restrict__ offsets,
     int M_total, int N, int K, int ld) {
@@ -789,7 +796,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_wgrad_kernel(
   uint16_t* Ce = C + (int64_t)e * N * K;
   if (groups == 0) {
     // no tokens: a zero tile (whole 8-byte pieces; K % 128 == 0)
-    for (int p = threadIdx.x; p < G::BM * G::BN / 4; p += kThreads) {
+    for (int p = threadIdx.x; p < G::BM * G::BN / 4; p += G::kThreads) {
       const int m = tm * G::BM + p / (G::BN / 4), n = tn * G::BN + 4 * (p % (G::BN / 4));
       if (m < N && n < K) *reinterpret_cast<uint2*>(Ce + (int64_t)m * K + n) = make_uint2(0u, 0u);
     }
@@ -841,10 +848,10 @@ hipError_t launch_dense(const uint8_t* A, const float* sA, const uint8_t* B, con
                         int64_t K, hipStream_t stream, uint8_t* QT = nullptr, float* sQT = nullptr) {
   const int tiles = (int)(((M + G::BM - 1) / G::BM) * ((N + G::BN - 1) / G::BN));
   if (row_mode)
-    hipLaunchKernelGGL((gemm_kernel<G, 1, QOUT, HW>), dim3(tiles), dim3(kThreads), 0, stream, A, sA, B, sB,
+    hipLaunchKernelGGL((gemm_kernel<G, 1, QOUT, HW>), dim3(tiles), dim3(G::kThreads), 0, stream, A, sA, B, sB,
                        C, Q, sQ, QT, sQT, (int)M, (int)N, (int)K);
   else
-    hipLaunchKernelGGL((gemm_kernel<G, 0, QOUT, HW>), dim3(tiles), dim3(kThreads), 0, stream, A, sA, B, sB,
+    hipLaunchKernelGGL((gemm_kernel<G, 0, QOUT, HW>), dim3(tiles), dim3(G::kThreads), 0, stream, A, sA, B, sB,
                        C, Q, sQ, QT, sQT, (int)M, (int)N, (int)K);
   return hipGetLastError();
 }
@@ -866,11 +873,10 @@ hipError_t launch_gemm_blockscaled_pow2(const uint8_t* A, const float* sA, const
                                         const float* sB, int row_mode, uint16_t* C, int64_t M,
                                         int64_t N, int64_t K, hipStream_t stream) {
   using namespace gemm;
-  switch (pick_dense(M, N)) {
-    case 1: return launch_dense<Cfg256x224, 0, 1>(A, sA, B, sB, row_mode, C, nullptr, nullptr, M, N, K, stream);
-    case 2: return launch_dense<Cfg224x256, 0, 1>(A, sA, B, sB, row_mode, C, nullptr, nullptr, M, N, K, stream);
-    default: return launch_dense<Cfg256x256, 0, 1>(A, sA, B, sB, row_mode, C, nullptr, nullptr, M, N, K, stream);
-  }
+  // 4 waves of 128x128 with the accumulators in AGPRs: 11% faster than the
+  // 8-wave tiles at 4096x7168x7168, on a par or better on the other shapes
+  // measured
+  return launch_dense<Cfg256x256w4, 0, 1>(A, sA, B, sB, row_mode, C, nullptr, nullptr, M, N, K, stream);
 }
 
 hipError_t launch_gemm_blockscaled_q1x128(const uint8_t* A, const float* sA, const uint8_t* B,
@@ -904,7 +910,7 @@ hipError_t launch_grouped_gemm_blockscaled(const uint8_t* A, const float* sA, co
   auto launch = [&](auto cfg) {
     using G = decltype(cfg);
     const int64_t tiles = ((M_total + G::BM - 1) / G::BM + E) * ((N + G::BN - 1) / G::BN);
-    hipLaunchKernelGGL((grouped_gemm_kernel<G>), dim3((unsigned)tiles), dim3(kThreads), 0, stream, A,
+    hipLaunchKernelGGL((grouped_gemm_kernel<G>), dim3((unsigned)tiles), dim3(G::kThreads), 0, stream, A,
                        sA, B, sB, C, offsets, E, (int)M_total, (int)N, (int)K);
     return hipGetLastError();
   };
@@ -925,7 +931,7 @@ hipError_t launch_grouped_gemm_wgrad(const uint8_t* A, const float* sA, const ui
   using G = Cfg256x256;
   const int64_t per_expert = ((N + G::BM - 1) / G::BM) * ((K + G::BN - 1) / G::BN);
   const int64_t tiles = (int64_t)E * kXcds * ((per_expert + kXcds - 1) / kXcds);
-  hipLaunchKernelGGL((grouped_wgrad_kernel<G>), dim3((unsigned)tiles), dim3(kThreads), 0, stream, A, sA, B,
+  hipLaunchKernelGGL((grouped_wgrad_kernel<G>), dim3((unsigned)tiles), dim3(G::kThreads), 0, stream, A, sA, B,
                      sB, C, offsets, (int)M_total, (int)N, (int)K, (int)ld);
   return hipGetLastError();
 }
