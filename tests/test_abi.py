@@ -113,6 +113,68 @@ def test_grouped_validation(L):
     assert f(NULL, NULL, NULL, NULL, NULL, NULL, 3, 0, 128, 128, NULL) == 0
 
 
+def test_pow2_entry_points_validate_like_their_counterparts(L):
+    assert L.fp8_quant_act_1x128_pow2(P, 2, 4, 128, P, P, NULL) == -4
+    assert L.fp8_quant_act_1x128_pow2(P, 1, 4, 100, P, P, NULL) == -2
+    assert L.fp8_quant_w_128x128_pow2(P, 1, 128, 128, P, P, P, NULL, NULL) == -5
+    assert L.fp8_quant_act_128x1_T_pow2(P, 1, 100, 64, P, P, NULL) == -2
+    assert L.fp8_gemm_blockscaled_pow2(P, P, P, P, 2, P, 4, 128, 128, NULL) == -5
+    assert L.fp8_gemm_blockscaled_pow2(P, P, P, P, 0, MIS, 4, 128, 128, NULL) == -3
+    assert L.fp8_gemm_blockscaled_pow2(NULL, NULL, NULL, NULL, 0, NULL, 0, 128, 128, NULL) == 0
+
+
+def test_fused_epilogue_validation(L):
+    f = L.fp8_gemm_blockscaled_q1x128
+    assert f(P, P, P, P, 3, P, P, 4, 128, 128, NULL) == -5
+    assert f(P, P, P, P, 0, P, P, 4, 100, 128, NULL) == -2
+    assert f(P, P, P, P, 0, NULL, P, 4, 128, 128, NULL) == -1
+    assert f(P, P, P, P, 0, P, MIS, 4, 128, 128, NULL) == -3
+    g = L.fp8_gemm_blockscaled_q1x128_q128x1T
+    assert g(P, P, P, P, 0, P, P, P, P, 100, 128, 128, NULL) == -2     # M not a multiple of 128
+    assert g(P, P, P, P, 0, P, P, NULL, P, 128, 128, 128, NULL) == -1
+    assert g(P, P, P, P, 0, P, P, P, MIS, 128, 128, 128, NULL) == -3
+    assert g(NULL, NULL, NULL, NULL, 0, NULL, NULL, NULL, NULL, 0, 128, 128, NULL) == 0
+
+
+def test_grouped_backward_validation(L):
+    q = L.fp8_quant_act_128x1_T_grouped
+    ld = fb.grouped_ld(300, 2)
+    assert q(P, 1, 300, 128, P, 2, ld - 128, P, P, NULL) == -2      # ld too small for the padding
+    assert q(P, 1, 300, 100, P, 2, ld, P, P, NULL) == -2            # C not a multiple of 128
+    assert q(P, 1, 300, 128, P, 0, ld, P, P, NULL) == -2            # rows but no experts
+    assert q(P, 3, 300, 128, P, 2, ld, P, P, NULL) == -4
+    assert q(P, 1, 300, 128, NULL, 2, ld, P, P, NULL) == -1
+    assert q(MIS, 1, 300, 128, P, 2, ld, P, P, NULL) == -3
+    assert q(NULL, 1, 0, 128, NULL, 2, fb.grouped_ld(0, 2), NULL, NULL, NULL) == 0   # no rows: no-op
+    w = L.fp8_grouped_gemm_wgrad
+    assert w(P, P, P, P, P, P, 2, 300, 128, 128, ld - 128, NULL) == -2
+    assert w(P, P, P, P, P, P, 2, 300, 100, 128, ld, NULL) == -2
+    assert w(P, P, P, P, NULL, P, 2, 300, 128, 128, ld, NULL) == -1
+    assert w(P, P, P, P, P, P, 2, 300, 1 << 20, 128, 1 << 12, NULL) == -7
+    assert w(NULL, NULL, NULL, NULL, NULL, NULL, 0, 0, 128, 128, 0, NULL) == 0
+    assert fb.grouped_ld(300, 2) == 640 and fb.grouped_ld(0, 0) == 0
+
+
+def test_dispatch_validation(L):
+    ws = L.fp8_moe_dispatch_workspace_bytes
+    assert ws(8192, 8, 32) == 4 * 32 * 64
+    assert ws(0, 8, 32) == 0
+    assert ws(10, 0, 4) < 0 and ws(10, 65, 4) < 0 and ws(10, 8, 0) < 0 and ws(10, 8, 1025) < 0
+    d = L.fp8_moe_dispatch
+    assert d(P, 1, 10, 100, P, 2, 4, P, P, P, P, P, P, NULL) == -2  # K not a multiple of 128
+    assert d(P, 7, 10, 128, P, 2, 4, P, P, P, P, P, P, NULL) == -4
+    assert d(P, 1, 10, 128, P, 2, 4, P, P, NULL, P, P, P, NULL) == -1
+    assert d(P, 1, 10, 128, P, 2, 4, P, P, P, P, P, NULL, NULL) == -1
+    assert d(MIS, 1, 10, 128, P, 2, 4, P, P, P, P, P, P, NULL) == -3
+    assert d(P, 1, 10, 128, P + 2, 2, 4, P, P, P, P, P, P, NULL) == -3   # int32 buffers 4-byte aligned
+    c = L.fp8_moe_combine
+    assert c(P, P, P, 10, 2, 12, P, NULL) == -2                      # N not a multiple of 8
+    assert c(P, P, P, 10, 0, 16, P, NULL) == -2
+    assert c(MIS, P, P, 10, 2, 16, P, NULL) == -3
+    assert c(P, NULL, P, 10, 2, 16, P, NULL) == -1
+    assert c(NULL, NULL, NULL, 0, 2, 16, NULL, NULL) == 0
+
+
 def test_binding_requires_gpu_tensors(L):
     import torch
     x = torch.zeros(4, 128)
