@@ -260,8 +260,9 @@ __global__ __launch_bounds__(256) void quant_act_128x1_T_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// 128x1 transposed quantizer for C % 8 == 0: one workgroup per (token group
-// g, 64 channels), 16-byte loads and an LDS transpose of the codes.
+// 128x1 transposed quantizer for C % 8 == 0, launched for F32 inputs (BF16
+// inputs take the wave kernel below): one workgroup per (token group g, 64
+// channels), 16-byte loads and an LDS transpose of the codes.
 // Lane l of wave w holds channels c0 + 8(l%8) .. +7 of tokens
 // 32w + 4(l/8) .. +3 of the group: each load instruction reads 8 whole
 // 128-byte token rows. Per-channel amax: a max over the lane's 4 tokens, then
@@ -345,6 +346,91 @@ __global__ __launch_bounds__(256) void quant_act_128x1_T_v8_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// 128x1 transposed quantizer for BF16 inputs with C % 8 == 0: one wave per
+// (token group g, 64 channels), no LDS and no barrier. Lane l holds channels
+// c0 + 8(l%8) .. +7 of the 16 consecutive tokens 16(l/8) .. +15 of the group:
+// load i reads token 16(l/8) + i, so each load instruction covers 8 whole
+// 128-byte token rows, and all 16 are issued before any compute. A channel's
+// amax is the max over the lane's 16 tokens, then over the 8 lanes sharing the
+// channel (lane bits 3..5: a DPP rotation by 8 within the 16-lane row, then
+// xor 16 and xor 32). Each lane then encodes its 16 tokens of each of its
+// channels, 16 consecutive bytes of a qT row, and stores them directly: one
+// store instruction writes 8 whole 128-byte pieces of qT rows.
+// (F32 inputs keep the kernel above: 8 F32 channels are 32 bytes, which would
+// split every load into two half-line requests.)
+// GROUPED and the group numbering as for the kernel above.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t word_of(const uint4& d, int k) {
+  return k == 0 ? d.x : k == 1 ? d.y : k == 2 ? d.z : d.w;
+}
+
+template <bool GROUPED, bool POW2>
+__global__ __launch_bounds__(256) void quant_act_128x1_T_wave_kernel(
+    const uint16_t* __restrict__ x, int64_t M, int C, uint8_t* __restrict__ qT, float* __restrict__ sT,
+    const int32_t* __restrict__ off, int E, int64_t ld) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int g = blockIdx.y;
+  int64_t row0 = (int64_t)g * kGroup;   // first input row of the group
+  int n_rows = kGroup;                  // its valid rows
+  if constexpr (GROUPED) {
+    const ExpertSlot es = locate_expert(off, E, (int)M, g, kGroup, 1);
+    if (es.e < 0) return;               // past the last group
+    row0 = es.r0 + (int64_t)kGroup * (g - es.base);
+    n_rows = min(kGroup, es.r1 - (int)row0);
+  }
+  const int c0 = (blockIdx.x * 4 + w) * 64;
+  if (c0 >= C) return;                  // no barrier below: a wave may leave alone
+  const int ch = c0 + 8 * (lane & 7);
+  const bool cok = ch < C;              // C % 8 == 0: all 8 channels valid or none
+  const int tb = 16 * (lane >> 3);      // first of the lane's 16 tokens
+
+  uint4 raw[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int r = GROUPED ? min(tb + i, n_rows - 1) : tb + i;
+    raw[i] = *reinterpret_cast<const uint4*>(x + (row0 + r) * C + (cok ? ch : 0));
+  }
+  // token tb + i, channel ch + j, widened exactly to FP32 (rows past the
+  // group's end read as zeros)
+  auto val = [&](int i, int j) {
+    const uint32_t d = word_of(raw[i], j >> 1);
+    const float f = __uint_as_float((j & 1) ? (d & 0xFFFF0000u) : (d << 16));
+    return GROUPED && tb + i >= n_rows ? 0.0f : f;
+  };
+  float sc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(val(i, j)));
+    m = fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0x128, 0xF, 0xF, false)));  // ror 8
+    m = fmaxf(m, __shfl_xor(m, 16, 64));
+    m = fmaxf(m, __shfl_xor(m, 32, 64));
+    sc[j] = scale_rule<POW2>(m);
+  }
+  // Widen again for the encoding rather than keep 128 widened values live:
+  // the packed loads take half the registers.
+#pragma unroll
+  for (int i = 0; i < 16; ++i) asm volatile("" : "+v"(raw[i].x), "+v"(raw[i].y), "+v"(raw[i].z), "+v"(raw[i].w));
+  if (lane < 8 && cok) {
+    float4* sp = reinterpret_cast<float4*>(sT + (int64_t)g * C + ch);
+    sp[0] = make_float4(sc[0], sc[1], sc[2], sc[3]);
+    sp[1] = make_float4(sc[4], sc[5], sc[6], sc[7]);
+  }
+  if (!cok) return;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const GroupDiv gd = div_of_scale_rule<true, POW2>(sc[j]);
+    uint32_t wd[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      wd[k] = pack4_rule<true, POW2>(val(4 * k, j), val(4 * k + 1, j), val(4 * k + 2, j), val(4 * k + 3, j), gd);
+    *reinterpret_cast<uint4*>(qT + (int64_t)(ch + j) * ld + (int64_t)g * kGroup + tb) =
+        make_uint4(wd[0], wd[1], wd[2], wd[3]);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Launchers (shapes validated by the C ABI layer).
 // ---------------------------------------------------------------------------
 hipError_t launch_quant_act_1x128(const void* x, bool bf16, bool pow2, int64_t M, int64_t K, uint8_t* q,
@@ -384,13 +470,21 @@ hipError_t launch_quant_act_128x1_T(const void* x, bool bf16, bool pow2, int64_t
   const dim3 grid((unsigned)((C + 63) / 64), (unsigned)(M / kGroup));
   using T = std::true_type;
   using F = std::false_type;
-  if (C % 8 == 0) {
-    auto go = [&](auto bf, auto p2) {
-      hipLaunchKernelGGL((quant_act_128x1_T_v8_kernel<decltype(bf)::value, false, decltype(p2)::value>), grid,
-                         dim3(256), 0, stream, x, M, (int)C, qT, sT, nullptr, 0, M);
+  if (C % 8 == 0 && bf16) {
+    const dim3 wgrid((unsigned)((C + 255) / 256), (unsigned)(M / kGroup));
+    auto go = [&](auto p2) {
+      hipLaunchKernelGGL((quant_act_128x1_T_wave_kernel<false, decltype(p2)::value>), wgrid, dim3(256), 0, stream,
+                         static_cast<const uint16_t*>(x), M, (int)C, qT, sT, nullptr, 0, M);
     };
-    if (bf16) pow2 ? go(T{}, T{}) : go(T{}, F{});
-    else pow2 ? go(F{}, T{}) : go(F{}, F{});
+    pow2 ? go(T{}) : go(F{});
+    return hipGetLastError();
+  }
+  if (C % 8 == 0) {
+    auto go = [&](auto p2) {
+      hipLaunchKernelGGL((quant_act_128x1_T_v8_kernel<false, false, decltype(p2)::value>), grid, dim3(256), 0,
+                         stream, x, M, (int)C, qT, sT, nullptr, 0, M);
+    };
+    pow2 ? go(T{}) : go(F{});
     return hipGetLastError();
   }
   auto go = [&](auto bf, auto pair, auto p2) {
@@ -409,8 +503,9 @@ hipError_t launch_quant_act_128x1_T_grouped(const void* x, bool bf16, int64_t M_
   // ld / 128 bounds the number of groups (validated: ld >= M_total + 127 E)
   const dim3 grid((unsigned)((C + 63) / 64), (unsigned)(ld / kGroup));
   if (bf16)
-    hipLaunchKernelGGL((quant_act_128x1_T_v8_kernel<true, true, false>), grid, dim3(256), 0, stream, x, M_total,
-                       (int)C, qT, sT, offsets, E, ld);
+    hipLaunchKernelGGL((quant_act_128x1_T_wave_kernel<true, false>), dim3((unsigned)((C + 255) / 256), grid.y),
+                       dim3(256), 0, stream, static_cast<const uint16_t*>(x), M_total, (int)C, qT, sT, offsets, E,
+                       ld);
   else
     hipLaunchKernelGGL((quant_act_128x1_T_v8_kernel<false, true, false>), grid, dim3(256), 0, stream, x, M_total,
                        (int)C, qT, sT, offsets, E, ld);
