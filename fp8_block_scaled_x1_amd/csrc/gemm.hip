@@ -438,14 +438,11 @@ __device__ __forceinline__ void run_tile(const Tile& t, uint8_t* smem) {
     v8i tf;
     Scales sc;
     read_chunk_start(0, hf, tf, sc);
-#ifndef CARRY
-#define CARRY 1
-#endif
     // Block mode carries the promotion of a chunk's last step into the first
     // step of the next chunk (zero partials before the first chunk), so every
     // step interleaves MFMAs with promotions; row mode, short of registers for
     // a second set of column scales, finishes it right after the barrier.
-    constexpr bool kCarry = CARRY && !ROW_MODE;
+    constexpr bool kCarry = !ROW_MODE;
     v4f p_prev[NH];
     Factors f_prev;
     if constexpr (kCarry) {
