@@ -588,20 +588,33 @@ __device__ __forceinline__ void run_tile(const Tile& t, uint8_t* smem) {
   const int m_lane = t.m0 + wm * WM + (lane & 15);
   const int n_lane = t.n0 + wn * WN + 4 * (lane >> 4);
   if constexpr (!QOUT) {
-    // BF16 epilogue, round to nearest even
+    // BF16 epilogue (round to nearest even) through LDS: each wave writes its
+    // values into a row-major copy of the tile in the operand slots, idle by
+    // now, and the workgroup then stores whole tile rows 16 bytes per lane
+    // (a wave's store covers 1 KB of consecutive row bytes instead of 16 rows
+    // x 32 bytes); 5-9% faster on the dense and grouped shapes measured.
+    constexpr int kPitch = G::BN * 2 + 16;   // tile row pitch in bytes
+    static_assert(G::BM * kPitch <= G::kLdsBytes, "the output tile fits the operand slots");
+    wait_and_barrier<0>();                   // every wave is done with the operand slots
+    const int r_lane = wm * WM + (lane & 15), c_lane = wn * WN + 4 * (lane >> 4);
 #pragma unroll
-    for (int i = 0; i < MS; ++i) {
-      const int m = m_lane + 16 * i;
-      if (m >= t.row_end) continue;
+    for (int i = 0; i < MS; ++i)
 #pragma unroll
       for (int j = 0; j < NS; ++j) {
-        const int n = n_lane + 16 * j;
-        if (n >= t.N) continue;
         uint2 o;
         o.x = float_to_bf16_bits(acc[i][j][0]) | (float_to_bf16_bits(acc[i][j][1]) << 16);
         o.y = float_to_bf16_bits(acc[i][j][2]) | (float_to_bf16_bits(acc[i][j][3]) << 16);
-        *reinterpret_cast<uint2*>(t.C + (int64_t)m * t.N + n) = o;
+        *reinterpret_cast<uint2*>(smem + (r_lane + 16 * i) * kPitch + 2 * (c_lane + 16 * j)) = o;
       }
+    wait_and_barrier<0>();
+    constexpr int kPieces = G::BN / 8;       // 16-byte pieces per tile row
+#pragma unroll 4
+    for (int p = tid; p < G::BM * kPieces; p += G::kThreads) {
+      const int row = p / kPieces, piece = p % kPieces;
+      const int m = t.m0 + row, n = t.n0 + 8 * piece;
+      if (m < t.row_end && n < t.N)
+        *reinterpret_cast<uint4*>(t.C + (int64_t)m * t.N + n) =
+            *reinterpret_cast<const uint4*>(smem + row * kPitch + 16 * piece);
     }
   } else {
     // Quantizing epilogue: the 1x128 quantizer applied to the BF16-rounded
