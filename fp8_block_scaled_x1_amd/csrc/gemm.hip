@@ -587,6 +587,7 @@ __device__ __forceinline__ void run_tile(const Tile& t, uint8_t* smem) {
   // lane holds C[m][n..n+3] of every MFMA tile
   const int m_lane = t.m0 + wm * WM + (lane & 15);
   const int n_lane = t.n0 + wn * WN + 4 * (lane >> 4);
+  const int r_lane = wm * WM + (lane & 15), c_lane = wn * WN + 4 * (lane >> 4);   // the same within the tile
   if constexpr (!QOUT) {
     // BF16 epilogue (round to nearest even) through LDS: each wave writes its
     // values into a row-major copy of the tile in the operand slots, idle by
@@ -596,7 +597,6 @@ __device__ __forceinline__ void run_tile(const Tile& t, uint8_t* smem) {
     constexpr int kPitch = G::BN * 2 + 16;   // tile row pitch in bytes
     static_assert(G::BM * kPitch <= G::kLdsBytes, "the output tile fits the operand slots");
     wait_and_barrier<0>();                   // every wave is done with the operand slots
-    const int r_lane = wm * WM + (lane & 15), c_lane = wn * WN + 4 * (lane >> 4);
 #pragma unroll
     for (int i = 0; i < MS; ++i)
 #pragma unroll
@@ -656,19 +656,29 @@ __device__ __forceinline__ void run_tile(const Tile& t, uint8_t* smem) {
         for (int w2 = 0; w2 < kGW; ++w2)
           ra[i] = fmaxf(ra[i], red[(wm * G::WGN + wn0 + w2) * WM + 16 * i + (lane & 15)]);
     }
+    // The codes go through LDS like the BF16 epilogue: a row-major copy of
+    // the tile's codes (and, for QOUT == 2, a column-major one), after the
+    // row maxima; rows of BN (BM) bytes with their 16-byte pieces XOR-swizzled
+    // by the row's low four bits, which keeps both the 4-byte writes and the
+    // 16-byte reads free of bank conflicts.
+    constexpr int kRedBytes = (G::kWaves * WM * 4 + 15) / 16 * 16;
+    constexpr int kQOff = kRedBytes, kQTOff = kQOff + G::BM * G::BN;
+    static_assert(kQTOff + (QOUT == 2 ? G::BN * G::BM : 0) <= G::kLdsBytes, "code tiles fit the operand slots");
+    static_assert(G::BN == 256 && (QOUT == 1 || G::BM == 256), "code tile rows of 16 pieces");
+    // byte offset of (row, col) in a code tile with rows of 256 bytes
+    auto swz_off = [](int row, int col) { return row * 256 + ((((col >> 4) ^ row) & 15) << 4) + (col & 15); };
+    if constexpr (kGW == 1) wait_and_barrier<0>();   // every wave is done with the operand slots
     const int grp = (t.n0 + wn * WN) / kGroup;
     const bool group_ok = t.n0 + wn * WN < t.N;   // N % 128 == 0: a group is wholly in or out
 #pragma unroll
     for (int i = 0; i < MS; ++i) {
       const int m = m_lane + 16 * i;
       const GroupDiv g = group_div<true>(ra[i]);   // the values are BF16 numbers
-      if (m < t.row_end && group_ok) {
 #pragma unroll
-        for (int j = 0; j < NS; ++j)
-          *reinterpret_cast<uint32_t*>(t.Q + (int64_t)m * t.N + n_lane + 16 * j) =
-              e4m3_div_pack4_t<true>(v[i][j][0], v[i][j][1], v[i][j][2], v[i][j][3], g);
-        if (lane < 16 && wn % kGW == 0) t.sQ[(int64_t)grp * t.row_end + m] = g.s;
-      }
+      for (int j = 0; j < NS; ++j)
+        *reinterpret_cast<uint32_t*>(smem + kQOff + swz_off(r_lane + 16 * i, c_lane + 16 * j)) =
+            e4m3_div_pack4_t<true>(v[i][j][0], v[i][j][1], v[i][j][2], v[i][j][3], g);
+      if (m < t.row_end && group_ok && lane < 16 && wn % kGW == 0) t.sQ[(int64_t)grp * t.row_end + m] = g.s;
     }
     if constexpr (QOUT == 2) {
       // 128x1 groups: a wave's WM = 128 rows are one group of each of its
@@ -711,10 +721,33 @@ __device__ __forceinline__ void run_tile(const Tile& t, uint8_t* smem) {
             const uint32_t sh = 8u * (uint32_t)q;
             const uint32_t out = ((w0 >> sh) & 0xFFu) | (((w1 >> sh) & 0xFFu) << 8) |
                                  (((w2 >> sh) & 0xFFu) << 16) | (((w3 >> sh) & 0xFFu) << 24);
-            const int m = m_grp0 + 16 * i + (lane & 12);
-            *reinterpret_cast<uint32_t*>(t.QT + (int64_t)n_col * t.row_end + m) = out;
+            *reinterpret_cast<uint32_t*>(smem + kQTOff + swz_off(n_col - t.n0, wm * WM + 16 * i + (lane & 12))) =
+                out;
           }
         }
+      }
+    }
+    wait_and_barrier<0>();   // the code tiles are complete
+    {
+      constexpr int kPieces = G::BN / 16;   // 16-byte pieces per code row
+#pragma unroll 4
+      for (int p = tid; p < G::BM * kPieces; p += G::kThreads) {
+        const int row = p / kPieces, piece = p % kPieces;
+        const int m = t.m0 + row, n = t.n0 + 16 * piece;
+        if (m < t.row_end && n < t.N)
+          *reinterpret_cast<uint4*>(t.Q + (int64_t)m * t.N + n) =
+              *reinterpret_cast<const uint4*>(smem + kQOff + swz_off(row, 16 * piece));
+      }
+    }
+    if constexpr (QOUT == 2) {
+      constexpr int kPieces = G::BM / 16;   // 16-byte pieces per transposed code row
+#pragma unroll 4
+      for (int p = tid; p < G::BN * kPieces; p += G::kThreads) {
+        const int col = p / kPieces, piece = p % kPieces;
+        const int n = t.n0 + col, m = t.m0 + 16 * piece;
+        if (n < t.N && m < t.row_end)
+          *reinterpret_cast<uint4*>(t.QT + (int64_t)n * t.row_end + m) =
+              *reinterpret_cast<const uint4*>(smem + kQTOff + swz_off(col, 16 * piece));
       }
     }
   }
