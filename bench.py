@@ -15,9 +15,12 @@ transposed 128x1 copy for the backward), and the Fprop with power-of-two
 scales applied by the MFMA itself (E8M0 variant).
 
 Prints one JSON line. `value` is whole-step throughput with inputs resident in
-HBM; `roofline` describes the dominant kernel, timed live with HIP events on
+HBM; `roofline` describes the dominant kernel, timed live with HIP events (created
+without the system-scope fence a default event performs on record) on
 the stream the kernels run on; `cpu_baseline` times the CPU oracle on a
-bounded sample of the same step (rank 0, one GPU only).
+bounded sample of the same step (rank 0, one GPU only). Before the warm-up
+steps, untimed steps run for --clock-ramp-ms (300 ms by default) so that the
+GPU clocks have reached their loaded steady state; `clock_ramp` reports them.
 """
 
 import argparse
@@ -59,19 +62,65 @@ def measured_traffic(kernel, workload):
     return ent.get("bytes_per_launch")
 
 
-class Timer:
-    """HIP events around each kernel of a step, on the current stream."""
+class HipTimingEvents:
+    """HIP events for timing only, created with hipEventDisableSystemFence.
 
-    def __init__(self, torch, names, steps):
-        self.torch = torch
+    A default HIP event performs a system-scope fence when it is recorded (an
+    L2 writeback and invalidation on MI355X), which slows the kernel that
+    follows it; the HIP headers recommend this flag for events that only
+    measure time. Calls go to the HIP runtime torch has loaded, so torch's
+    stream handles are valid here.
+    """
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self, torch):
+        import ctypes
+        self.ctypes = ctypes
+        path = os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so")
+        self.hip = ctypes.CDLL(path if os.path.exists(path) else "libamdhip64.so")
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self):
+        e = self.ctypes.c_void_p()
+        rc = self.hip.hipEventCreateWithFlags(self.ctypes.byref(e), self.DISABLE_SYSTEM_FENCE)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+        return e
+
+    def record(self, e, stream):
+        rc = self.hip.hipEventRecord(e, stream)
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def elapsed_ms(self, a, b):
+        ms = self.ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(self.ctypes.byref(ms), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def destroy(self, e):
+        self.hip.hipEventDestroy(e)
+
+
+class Timer:
+    """Timing events around each kernel of a step, on the stream the kernels run on."""
+
+    def __init__(self, torch, names, steps, stream, events):
         self.names = names
-        self.ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(steps)]
+        self.stream = stream
+        self.events = events
+        self.ev = [[events.create() for _ in range(len(names) + 1)] for _ in range(steps)]
         self.i = 0
         self.k = 0
 
     def mark(self):
         if self.i < len(self.ev):
-            self.ev[self.i][self.k].record()
+            self.events.record(self.ev[self.i][self.k], self.stream)
         self.k += 1
         if self.k == len(self.names) + 1:
             self.k = 0
@@ -80,9 +129,15 @@ class Timer:
     def averages_us(self):
         out = {}
         for j, n in enumerate(self.names):
-            ts = [row[j].elapsed_time(row[j + 1]) * 1e3 for row in self.ev[:self.i]]
+            ts = [self.events.elapsed_ms(row[j], row[j + 1]) * 1e3 for row in self.ev[:self.i]]
             out[n] = sum(ts) / len(ts)
         return out
+
+    def close(self):
+        for row in self.ev:
+            for e in row:
+                self.events.destroy(e)
+        self.ev = []
 
 
 # ---------------------------------------------------------------------------
@@ -587,10 +642,13 @@ def cpu_baseline(workload):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", choices=sorted(WORKLOADS), default="dense_fprop")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--clock-ramp-ms", type=float, default=300.0,
+                    help="untimed steps for this long before the warm-up steps, so that the GPU clocks "
+                         "reach their loaded steady state (0 to skip)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -608,11 +666,23 @@ def main():
     step, info = WORKLOADS[args.workload](torch, fb, dev)
     names = info["names"]
 
-    warm = Timer(torch, names, 0)
+    events = HipTimingEvents(torch)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    warm = Timer(torch, names, 0, stream, events)
+    # The MI355X raises its clocks over the first ~100 ms under load: a few
+    # warm-up steps alone leave the timed steps at ramp-up clocks (the dense
+    # GEMM measured 15% slower). Untimed steps for --clock-ramp-ms come first.
+    ramp_steps, t_ramp = 0, time.perf_counter()
+    while (time.perf_counter() - t_ramp) * 1e3 < args.clock_ramp_ms and ramp_steps < 20000:
+        for _ in range(4):
+            step(warm)
+        ramp_steps += 4
+        torch.cuda.synchronize()
+    ramp_ms = (time.perf_counter() - t_ramp) * 1e3
     for _ in range(args.warmup):
         step(warm)
     torch.cuda.synchronize()
-    timer = Timer(torch, names, args.steps)
+    timer = Timer(torch, names, args.steps, stream, events)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
@@ -622,6 +692,7 @@ def main():
     ms_per_step = (t1 - t0) * 1e3 / args.steps
 
     per_kernel = timer.averages_us()
+    timer.close()
     kernels = {}
     for n in names:
         unit, work = info["work"][n]
@@ -649,6 +720,7 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3 (fp32 accumulate, bf16 out)",
         "data": "synthetic (seeded; shapes and distributions of the workload)",
         "config": info["config"], "kernels": kernels, "roofline": roofline,
+        "clock_ramp": {"steps": ramp_steps, "ms": round(ramp_ms, 1)},
     }
     if not args.no_cpu_baseline and args.workload != "copy":
         line["cpu_baseline"] = cpu_baseline(args.workload)
