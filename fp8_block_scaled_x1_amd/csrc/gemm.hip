@@ -86,9 +86,6 @@ struct Cfg {
 using Cfg256x256 = Cfg<256, 256, 2, 4, 2, 2>;
 using Cfg256x224 = Cfg<256, 224, 4, 2, 3, 2>;
 using Cfg224x256 = Cfg<224, 256, 2, 4, 2, 3>;
-// 128x256, waves 2x4 of 64x64, both operands three deep: grouped GEMMs with
-// few rows per group (decode), where B is the operand streamed from HBM
-using Cfg128x256d = Cfg<128, 256, 2, 4, 3, 3>;
 // 256x256 with 4 waves of 128x128 (one per SIMD, up to 512 registers each):
 // only for the hardware-scaled variant, whose accumulators the MFMA updates
 // in place (they can live in AGPRs), so no promotion needs them in VGPRs
@@ -899,6 +896,206 @@ hipError_t launch_dense(const uint8_t* A, const float* sA, const uint8_t* B, con
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Decode-shaped grouped GEMM (few activation rows per expert, so the weights
+// are the stream). One workgroup per (expert, 128 weight rows) covers all of
+// the expert's rows, up to 256 per pass, so every weight byte is read once
+// (experts with more rows take further passes). Each of the 8 waves streams
+// its own 16 weight rows from HBM straight into MFMA operand registers, kDB
+// chunks ahead of use. The activation chunk (the pass's rows x 128 bytes and
+// their sA) goes through registers into a double-buffered, swizzled LDS tile
+// shared by the waves, one chunk ahead, with one barrier per chunk. Every load
+// is an ordinary vector load, so the compiler's own waits stay exact; the
+// barrier waits for LDS only and leaves the weight loads in flight. A pass
+// computes NSUB activation subtiles of 16 rows (its rows rounded up to 32),
+// compiled once per NSUB so no subtile branches sit in the chunk loop. The
+// operands are swapped as in the tile kernel: lane l holds
+// C[m = 16i + l%16][n .. n+3].
+// ---------------------------------------------------------------------------
+namespace dec {
+constexpr int kWaves = 8, kThreads = 64 * kWaves;
+constexpr int kBM = 256;                     // activation rows per pass
+constexpr int kBN = 16 * kWaves;             // weight rows per workgroup, 16 per wave
+constexpr int kDB = 4;                       // weight chunks loaded ahead of the one in use
+constexpr int kR = kDB + 1;                  // weight register ring
+constexpr int kASlot = kBM * BK + kBM * 4;   // codes, then the chunk's sA vector
+constexpr int kPitch = kBN * 2 + 16;         // epilogue tile row pitch (bytes)
+constexpr int kLds = (2 * kASlot > kBM * kPitch) ? 2 * kASlot : kBM * kPitch;
+
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+struct Pass {
+  const uint8_t* A;     // activation codes [M_total][K]
+  const float* sA;      // [K/128][M_total]
+  uint16_t* C;          // [M_total][N]
+  const uint8_t* brow;  // this lane's weight fragment row (+ its 32-byte K offset)
+  const float* sbp;     // sB of this wave's 128-row scale block, one value per chunk
+  int M_total, N, K, nkb, m0, rows, n_col0;
+};
+
+template <int NSUB>
+__device__ __forceinline__ void run_pass(const Pass a, uint8_t* smem) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nkb = a.nkb, rows = a.rows;
+
+  // Activation staging: thread t loads 16-byte piece t%8 of rows t/8 + 64q for
+  // the kQ rounds that cover the pass's NSUB*16 rows (rows past those in the
+  // last round are skipped; rows past the expert's end are clamped, and their
+  // results never stored). Named registers written out per round: an array
+  // indexed in a loop was left in scratch.
+  constexpr int kRowsP = NSUB * 16, kRR = kThreads / 8, kQ = (kRowsP + kRR - 1) / kRR;
+  static_assert(kQ <= 4 && kRowsP <= kThreads, "staging rounds; one sA value per thread");
+  const int ar = tid >> 3, ap = tid & 7;
+  uint4 ast0, ast1, ast2, ast3;
+  float sst = 0.0f;
+  const uint8_t* abase = a.A + (int64_t)a.m0 * a.K + 16 * ap;
+  const float* srow = a.sA + a.m0 + min(tid, rows - 1);
+#define FP8BS_DEC_LD(q)                                                                              \
+  if constexpr (kQ > q) {                                                                            \
+    if (q + 1 < kQ || ar + kRR * q < kRowsP)                                                         \
+      ast##q = *reinterpret_cast<const uint4*>(abase + o + (int64_t)min(ar + kRR * q, rows - 1) * a.K); \
+  }
+#define FP8BS_DEC_ST(q)                                                                              \
+  if constexpr (kQ > q) {                                                                            \
+    const int r = ar + kRR * q;                                                                      \
+    if (q + 1 < kQ || r < kRowsP) *reinterpret_cast<uint4*>(base + r * BK + ((ap ^ swz(r)) << 4)) = ast##q; \
+  }
+  auto a_load = [&](int kb) {
+    const int64_t o = (int64_t)kb * BK;
+    FP8BS_DEC_LD(0) FP8BS_DEC_LD(1) FP8BS_DEC_LD(2) FP8BS_DEC_LD(3)
+    if (tid < kRowsP) sst = srow[(int64_t)kb * a.M_total];
+  };
+  auto a_store = [&](int slot) {
+    uint8_t* base = smem + slot * kASlot;
+    FP8BS_DEC_ST(0) FP8BS_DEC_ST(1) FP8BS_DEC_ST(2) FP8BS_DEC_ST(3)
+    if (tid < kRowsP) reinterpret_cast<float*>(base + kBM * BK)[tid] = sst;
+  };
+#undef FP8BS_DEC_LD
+#undef FP8BS_DEC_ST
+
+  // weight ring: chunk c in registers bq[c % kR], its block scale in sbq
+  v8i bq[kR];
+  float sbq[kR];
+  auto b_load = [&](int c, int u) {
+    const int cc = min(c, nkb - 1);
+    bq[u] = *reinterpret_cast<const v8i*>(a.brow + (int64_t)cc * BK);
+    sbq[u] = a.sbp[cc];
+  };
+  v4f acc[NSUB];
+#pragma unroll
+  for (int i = 0; i < NSUB; ++i) acc[i] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  // prologue: weights 0 .. kDB-1, activations 0 (in LDS) and 1 (staged)
+#pragma unroll
+  for (int u = 0; u < kDB; ++u) b_load(u, u);
+  a_load(0);
+  a_store(0);
+  a_load(min(1, nkb - 1));
+  lds_barrier();
+
+  // Chunk kb with its weights in ring slot u: fragment i+1 is read while MFMA
+  // i runs, and MFMA i's partial is promoted one subtile later. Each promoted
+  // accumulator is pinned where it is computed (otherwise the compiler sinks
+  // the promotions to the accumulators' next use and keeps every partial).
+  auto chunk = [&](int kb, int u) {
+    b_load(kb + kDB, (u + kDB) % kR);
+    const uint8_t* slot = smem + (kb & 1) * kASlot;
+    const float* sAs = reinterpret_cast<const float*>(slot + kBM * BK) + (lane & 15);
+    v8i af = read_frag(slot, 0, lane);
+    v4f pp = v4f{0.f, 0.f, 0.f, 0.f};
+    float fp = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NSUB; ++i) {
+      const v8i a_now = af;
+      if (i + 1 < NSUB) af = read_frag(slot, i + 1, lane);
+      const float f_now = sAs[16 * i] * sbq[u];
+      const v4f pc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bq[u], a_now, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0,
+                                                                       0, 0, 0, 0);
+      if (i > 0) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[i - 1][r] = fmaf(pp[r], fp, acc[i - 1][r]);
+        asm volatile("" : "+v"(acc[i - 1]));
+      }
+      pp = pc;
+      fp = f_now;
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[NSUB - 1][r] = fmaf(pp[r], fp, acc[NSUB - 1][r]);
+    asm volatile("" : "+v"(acc[NSUB - 1]));
+    if (kb + 1 < nkb) {   // activations kb+1 into the other slot, then the loads of kb+2
+      a_store((kb + 1) & 1);
+      a_load(min(kb + 2, nkb - 1));
+    }
+    lds_barrier();
+  };
+  int kb = 0;
+  for (; kb + kR <= nkb; kb += kR) {
+#pragma unroll
+    for (int u = 0; u < kR; ++u) chunk(kb + u, u);
+  }
+#pragma unroll
+  for (int u = 0; u < kR; ++u)
+    if (kb + u < nkb) chunk(kb + u, u);
+
+  // epilogue through LDS: row-major BF16 tile [NSUB*16][kBN], whole rows out
+#pragma unroll
+  for (int i = 0; i < NSUB; ++i) {
+    uint2 o;
+    o.x = float_to_bf16_bits(acc[i][0]) | (float_to_bf16_bits(acc[i][1]) << 16);
+    o.y = float_to_bf16_bits(acc[i][2]) | (float_to_bf16_bits(acc[i][3]) << 16);
+    const int r = 16 * i + (lane & 15), c = 16 * wave + 4 * (lane >> 4);
+    *reinterpret_cast<uint2*>(smem + r * kPitch + 2 * c) = o;
+  }
+  lds_barrier();
+  constexpr int kPieces = kBN / 8;
+  for (int p = tid; p < kRowsP * kPieces; p += kThreads) {
+    const int row = p / kPieces, piece = p % kPieces;
+    const int n = a.n_col0 + 8 * piece;
+    if (row < rows && n < a.N)
+      *reinterpret_cast<uint4*>(a.C + (int64_t)(a.m0 + row) * a.N + n) =
+          *reinterpret_cast<const uint4*>(smem + row * kPitch + 16 * piece);
+  }
+  lds_barrier();   // the next pass reuses the LDS
+}
+}  // namespace dec
+
+__global__ __launch_bounds__(dec::kThreads, 1) void grouped_decode_kernel(
+    const uint8_t* __restrict__ A, const float* __restrict__ sA, const uint8_t* __restrict__ B,
+    const float* __restrict__ sB, uint16_t* __restrict__ C, const int32_t* __restrict__ offsets, int E,
+    int M_total, int N, int K) {
+  __shared__ __align__(16) uint8_t smem[dec::kLds];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nblk = (N + dec::kBN - 1) / dec::kBN;
+  const int e = blockIdx.x / nblk, nb = blockIdx.x % nblk;
+  const int r0 = min(max(offsets[e], 0), M_total);
+  const int r1 = min(max(offsets[e + 1], r0), M_total);
+  if (r1 <= r0) return;                            // no rows: nothing to write
+  dec::Pass a;
+  a.A = A; a.sA = sA; a.C = C; a.M_total = M_total; a.N = N; a.K = K; a.nkb = K / BK;
+  a.n_col0 = nb * dec::kBN;
+  const int nw0 = a.n_col0 + 16 * wave;            // this wave's first weight row
+  a.brow = B + (int64_t)e * N * K + (int64_t)min(nw0 + (lane & 15), N - 1) * K + 32 * (lane >> 4);
+  // the wave's 16 rows lie in one 128-row scale block
+  a.sbp = sB + (int64_t)e * (N / BK) * a.nkb + (int64_t)(min(nw0, N - 1) / BK) * a.nkb;
+  for (int m0 = r0; m0 < r1; m0 += dec::kBM) {
+    a.m0 = m0;
+    a.rows = min(dec::kBM, r1 - m0);
+    switch ((a.rows + 31) / 32) {
+      case 1: dec::run_pass<2>(a, smem); break;
+      case 2: dec::run_pass<4>(a, smem); break;
+      case 3: dec::run_pass<6>(a, smem); break;
+      case 4: dec::run_pass<8>(a, smem); break;
+      case 5: dec::run_pass<10>(a, smem); break;
+      case 6: dec::run_pass<12>(a, smem); break;
+      case 7: dec::run_pass<14>(a, smem); break;
+      default: dec::run_pass<16>(a, smem); break;
+    }
+  }
+}
+
 }  // namespace gemm
 
 hipError_t launch_gemm_blockscaled(const uint8_t* A, const float* sA, const uint8_t* B,
@@ -957,12 +1154,14 @@ hipError_t launch_grouped_gemm_blockscaled(const uint8_t* A, const float* sA, co
                        sA, B, sB, C, offsets, E, (int)M_total, (int)N, (int)K);
     return hipGetLastError();
   };
-  // Few rows per expert on average (decode): half-height tiles waste fewer
-  // MFMAs on padding rows while each expert's weights are still read about
-  // once, and both operands three deep keep two chunks of weights in flight
-  // (the weights stream from HBM; a two-deep ring leaves every chunk waiting
-  // out a full HBM latency).
-  if (M_total < (int64_t)E * 256) return launch(Cfg128x256d{});
+  // Few rows per expert on average (decode): the weight-streaming kernel,
+  // which reads every expert's weights once whatever its rows
+  if (M_total < (int64_t)E * 256) {
+    const int64_t blocks = (int64_t)E * ((N + dec::kBN - 1) / dec::kBN);
+    hipLaunchKernelGGL(grouped_decode_kernel, dim3((unsigned)blocks), dim3(dec::kThreads), 0, stream, A, sA, B, sB,
+                       C, offsets, E, (int)M_total, (int)N, (int)K);
+    return hipGetLastError();
+  }
   return launch(Cfg256x256{});
 }
 

@@ -133,6 +133,7 @@ def _grouped_case(dev, counts, N, K, seed):
     ([5], 128, 128),
     ([0, 1, 0, 300, 17, 0], 256, 256),
     ([256, 255, 257, 1], 384, 384),
+    ([17, 0, 130, 64, 2, 33], 640, 896),
     ([1000, 3, 600], 512, 1024),
 ])
 def test_grouped_gemm_random(dev, counts, N, K):
