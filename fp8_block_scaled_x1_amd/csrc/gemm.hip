@@ -1069,7 +1069,10 @@ __global__ __launch_bounds__(dec::kThreads, 1) void grouped_decode_kernel(
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nblk = (N + dec::kBN - 1) / dec::kBN;
-  const int e = blockIdx.x / nblk, nb = blockIdx.x % nblk;
+  // consecutive ids on one XCD: an expert's weight blocks share that XCD's L2
+  // copy of its activations instead of every XCD fetching them
+  const int pid = xcd_remap(blockIdx.x, gridDim.x);
+  const int e = pid / nblk, nb = pid % nblk;
   const int r0 = min(max(offsets[e], 0), M_total);
   const int r1 = min(max(offsets[e + 1], r0), M_total);
   if (r1 <= r0) return;                            // no rows: nothing to write
