@@ -9,7 +9,8 @@
 // On one GPU the dispatch target is the grouped GEMM itself: the payload is
 // written directly in its layout, rows sorted by expert and, inside an
 // expert, by (token, slot) -- the order a stable sort by expert gives:
-//   route:     per-block expert histograms, one scan, stable in-block ranks
+//   route:     per-block expert histograms, their scan (inside the rank
+//              kernel for small tables), stable in-block ranks
 //              -> offsets[E+1], pos[T][topk] (row of each token copy),
 //                 src[T*topk] (token of each row);
 //   dispatch:  each token row is read once, quantized 1x128 (the arithmetic of
@@ -119,20 +120,81 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(int32_t* __restrict__ 
   }
 }
 
-// Stable ranks: pair i of block b goes to row ws[b][e] + (pairs of block b
-// before i with the same expert e). The block takes its pairs in four rounds
-// of 256 consecutive pairs; inside a wave the pairs with the same expert are
-// found with one ballot per bit of the expert id; the waves' counts meet in
-// LDS, and a per-expert cursor carries the count over the rounds.
+// Stable ranks: pair i of block b goes to row first(b, e) + (pairs of block
+// b before i with the same expert e), first(b, e) being the first row of block
+// b's pairs of expert e. Without FUSED, route_scan_kernel has already turned
+// ws[b][e] into first(b, e). With FUSED (small tables: blocks x experts <=
+// kFusedScanMax) ws holds the raw histograms and every block forms its own
+// first(., e) from the whole table (all blocks' counts for the experts'
+// offsets, its predecessors' for its own position), which saves the scan's
+// launch; block 0 also writes offsets. The block takes its pairs in four
+// rounds of 256 consecutive pairs; inside a wave the pairs with the same
+// expert are found with one ballot per bit of the expert id; the waves'
+// counts meet in LDS, and a per-expert cursor carries the count over the
+// rounds.
+constexpr int kFusedScanMax = 16384;
+
+template <bool FUSED>
 __global__ __launch_bounds__(kRouteThreads) void route_rank_kernel(const int32_t* __restrict__ ids, int64_t P,
                                                                     int E, int topk,
-                                                                    const int32_t* __restrict__ ws,
+                                                                    const int32_t* __restrict__ ws, int nblocks,
+                                                                    int32_t* __restrict__ offsets,
                                                                     int32_t* __restrict__ pos,
                                                                     int32_t* __restrict__ src) {
   __shared__ int cursor[kMaxExperts];
   __shared__ int cnt[4][kMaxExperts];
+  __shared__ int wsum[kRouteThreads / 64];
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  for (int e = t; e < E; e += kRouteThreads) cursor[e] = ws[(int64_t)blockIdx.x * E + e];
+  if constexpr (FUSED) {
+    // per expert: every block's pairs (cnt[0]) and this block's predecessors' (cursor)
+    for (int e = t; e < E; e += kRouteThreads) {
+      int all = 0, before = 0;
+      for (int b0 = 0; b0 < nblocks; b0 += kScanBatch) {
+        int c[kScanBatch];
+#pragma unroll
+        for (int u = 0; u < kScanBatch; ++u) c[u] = b0 + u < nblocks ? ws[(int64_t)(b0 + u) * E + e] : 0;
+#pragma unroll
+        for (int u = 0; u < kScanBatch; ++u) {
+          all += c[u];
+          if (b0 + u < (int)blockIdx.x) before += c[u];
+        }
+      }
+      cnt[0][e] = all;
+      cursor[e] = before;
+    }
+    __syncthreads();
+    // exclusive scan of the experts' totals: thread t holds experts 4t .. 4t+3
+    static_assert(4 * kRouteThreads >= kMaxExperts, "four experts per thread");
+    int v[4], sum = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      v[k] = 4 * t + k < E ? cnt[0][4 * t + k] : 0;
+      sum += v[k];
+    }
+    int incl = sum;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int x = __shfl_up(incl, d, 64);
+      if (lane >= d) incl += x;
+    }
+    if (lane == 63) wsum[w] = incl;
+    __syncthreads();
+    int run = incl - sum;
+    for (int k = 0; k < w; ++k) run += wsum[k];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int e = 4 * t + k;
+      if (e < E) {
+        cursor[e] += run;
+        if (blockIdx.x == 0) offsets[e] = run;
+      }
+      run += v[k];
+    }
+    if (blockIdx.x == 0 && t == kRouteThreads - 1) offsets[E] = run;   // every pair: P
+    __syncthreads();   // cnt is reused below
+  } else {
+    for (int e = t; e < E; e += kRouteThreads) cursor[e] = ws[(int64_t)blockIdx.x * E + e];
+  }
   int bits = 0;
   while ((1 << bits) < E) ++bits;
   const int64_t first = (int64_t)blockIdx.x * kRouteChunk;
@@ -282,10 +344,19 @@ hipError_t launch_moe_dispatch(const void* x, bool bf16, int64_t T, int64_t K, c
                                int32_t* ws, hipStream_t stream) {
   const int64_t P = T * topk;
   const int nb = (int)moe_route_blocks(P);
-  if (nb > 0) hipLaunchKernelGGL(route_hist_kernel, dim3(nb), dim3(kRouteThreads), 0, stream, ids, P, E, ws);
-  hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(1024), 0, stream, ws, nb, E, offsets);
-  if (nb == 0) return hipGetLastError();   // no tokens: offsets all zero
-  hipLaunchKernelGGL(route_rank_kernel, dim3(nb), dim3(kRouteThreads), 0, stream, ids, P, E, topk, ws, pos, src);
+  if (nb == 0) {   // no tokens: offsets all zero
+    hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(1024), 0, stream, ws, nb, E, offsets);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(route_hist_kernel, dim3(nb), dim3(kRouteThreads), 0, stream, ids, P, E, ws);
+  if ((int64_t)nb * E <= kFusedScanMax) {
+    hipLaunchKernelGGL(route_rank_kernel<true>, dim3(nb), dim3(kRouteThreads), 0, stream, ids, P, E, topk, ws, nb,
+                       offsets, pos, src);
+  } else {
+    hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(1024), 0, stream, ws, nb, E, offsets);
+    hipLaunchKernelGGL(route_rank_kernel<false>, dim3(nb), dim3(kRouteThreads), 0, stream, ids, P, E, topk, ws, nb,
+                       offsets, pos, src);
+  }
   if (K == 0) return hipGetLastError();
   const dim3 grid = row_grid((K / kGroup + 3) / 4, 8, T);
   if (bf16)

@@ -46,7 +46,7 @@ def _check_dispatch(dev, x, ids, E, what):
 
 @pytest.mark.parametrize("T,K,topk,E", [
     (1, 128, 1, 1), (37, 256, 4, 8), (200, 384, 8, 32), (1000, 128, 8, 256), (1500, 128, 2, 1024),
-    (2049, 256, 6, 9),
+    (2049, 256, 6, 9), (2200, 128, 8, 1024),
 ])
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 def test_dispatch_random(dev, T, K, topk, E, dtype):
