@@ -549,6 +549,14 @@ __device__ __forceinline__ void run_tile(const Tile& t, uint8_t* smem) {
                                                                        acc[i][j], 0, 0, 0, eb[j], 0, ea[i]);
         }
         if (t + 1 < NT) tf = read_t(kb, t + 1);
+        // one MFMA, then the next step's fragment reads, then the other MFMAs:
+        // with one wave per SIMD, reads issued after all of a step's MFMAs
+        // land after the next step wants them (5-8% slower)
+        if (t + 1 < NT) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, NH - 1, 0);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
       barrier(kb + 1);
