@@ -134,6 +134,8 @@ def _grouped_case(dev, counts, N, K, seed):
     ([0, 1, 0, 300, 17, 0], 256, 256),
     ([256, 255, 257, 1], 384, 384),
     ([17, 0, 130, 64, 2, 33], 640, 896),
+    ([600, 1, 0, 1], 256, 512),                                      # one expert in three 256-row passes
+    ([int(c) for c in np.random.default_rng(5).integers(0, 9, 200) * (np.arange(200) % 3 != 0)], 384, 256),
     ([1000, 3, 600], 512, 1024),
 ])
 def test_grouped_gemm_random(dev, counts, N, K):
