@@ -136,6 +136,7 @@ def _grouped_case(dev, counts, N, K, seed):
     ([17, 0, 130, 64, 2, 33], 640, 896),
     ([600, 1, 0, 1], 256, 512),                                      # one expert in three 256-row passes
     ([int(c) for c in np.random.default_rng(5).integers(0, 9, 200) * (np.arange(200) % 3 != 0)], 384, 256),
+    ([int(c) for c in np.random.default_rng(6).integers(0, 5, 300)], 128, 256),   # > 256 experts: index order
     ([1000, 3, 600], 512, 1024),
 ])
 def test_grouped_gemm_random(dev, counts, N, K):
