@@ -124,8 +124,10 @@ def _grouped_case(dev, counts, N, K, seed):
     sA = _scales((K // 128, M), seed + 1)
     B = _codes((E, N, K), seed + 2)
     sB = _scales((E, N // 128, K // 128), seed + 3)
-    C = fb.fp8_grouped_gemm_blockscaled(A.to(dev), sA.to(dev), B.to(dev), sB.to(dev),
-                                        torch.from_numpy(off).to(dev))
+    # NaN-filled output: a row the kernel does not write fails the bound
+    C = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=dev)
+    fb.fp8_grouped_gemm_blockscaled(A.to(dev), sA.to(dev), B.to(dev), sB.to(dev), torch.from_numpy(off).to(dev),
+                                    out=C)
     return A, sA, B, sB, off, C
 
 
@@ -155,8 +157,10 @@ def test_grouped_gemm_decode_workload(dev):
     sw = torch.empty((E, N // 128, K // 128), dtype=torch.float32, device=dev)
     for e in range(E):
         qw[e], sw[e] = fb.fp8_quant_w_128x128(d["W"][e])
-    C = fb.fp8_grouped_gemm_blockscaled(qa, sa, qw, sw, torch.from_numpy(off).to(dev))
+    C = torch.full((int(off[-1]), N), float("nan"), dtype=torch.bfloat16, device=dev)
+    fb.fp8_grouped_gemm_blockscaled(qa, sa, qw, sw, torch.from_numpy(off).to(dev), out=C)
     torch.cuda.synchronize()
+    assert not torch.isnan(C).any(), "rows left unwritten"
     # first and last row of every expert
     rows = np.unique(np.concatenate([off[:-1], off[1:] - 1]))
     ref, absref = oracle.grouped_gemm_ref(u8(qa), sa.cpu().numpy(), u8(qw), sw.cpu().numpy(), off, rows=rows)
