@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libfp8bs.so")
 
 F32, BF16 = 0, 1
 SCALE_BLOCK128, SCALE_ROW = 0, 1
-ABI_VERSION = 6
+ABI_VERSION = 7
 
 _c_int64 = ctypes.c_int64
 _vp = ctypes.c_void_p
@@ -27,6 +27,8 @@ _SIGNATURES = {
     "fp8_quant_w_128x128": [_vp, ctypes.c_int, _c_int64, _c_int64, _vp, _vp, _vp, _vp, _vp],
     "fp8_quant_act_128x1_T": [_vp, ctypes.c_int, _c_int64, _c_int64, _vp, _vp, _vp],
     "fp8_gemm_blockscaled": [_vp, _vp, _vp, _vp, ctypes.c_int, _vp, _c_int64, _c_int64, _c_int64, _vp],
+    "fp8_gemm_blockscaled_tile": [_c_int64, _c_int64, _c_int64, ctypes.c_int, ctypes.POINTER(ctypes.c_int),
+                                  ctypes.POINTER(ctypes.c_int)],
     "fp8_quant_act_1x128_pow2": [_vp, ctypes.c_int, _c_int64, _c_int64, _vp, _vp, _vp],
     "fp8_quant_w_128x128_pow2": [_vp, ctypes.c_int, _c_int64, _c_int64, _vp, _vp, _vp, _vp, _vp],
     "fp8_quant_act_128x1_T_pow2": [_vp, ctypes.c_int, _c_int64, _c_int64, _vp, _vp, _vp],
@@ -175,15 +177,23 @@ def fp8_gemm_blockscaled(A, sA, B, sB, b_scale_mode=SCALE_BLOCK128, out=None, po
     """C[M][N] (bf16) = block-scaled FP8 GEMM of A[M][K] and B[N][K] (both K-contiguous).
 
     pow2: the scales are powers of two and the MFMA applies them (E8M0)."""
+    if out is not None and tuple(out.shape) != (A.shape[0], B.shape[0]):
+        raise ValueError("out has the wrong shape")
     M, N, K, (pa, psa, pb, psb) = _gemm_operands(A, sA, B, sB, b_scale_mode)
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
     pc = _dev(out, "out", (torch.bfloat16,))
-    if tuple(out.shape) != (M, N):
-        raise ValueError("out has the wrong shape")
     fn = "fp8_gemm_blockscaled_pow2" if pow2 else "fp8_gemm_blockscaled"
     _check(fn, getattr(lib(), fn)(pa, psa, pb, psb, int(b_scale_mode), pc, M, N, K, _stream(A)))
     return out
+
+
+def fp8_gemm_blockscaled_tile(M, N, K, b_scale_mode=SCALE_BLOCK128):
+    """(rows, columns) of the output tile fp8_gemm_blockscaled uses for this shape."""
+    bm, bn = ctypes.c_int(), ctypes.c_int()
+    _check("fp8_gemm_blockscaled_tile",
+           lib().fp8_gemm_blockscaled_tile(M, N, K, int(b_scale_mode), ctypes.byref(bm), ctypes.byref(bn)))
+    return bm.value, bn.value
 
 
 def fp8_gemm_blockscaled_q1x128(A, sA, B, sB, b_scale_mode=SCALE_BLOCK128):
@@ -223,6 +233,8 @@ def fp8_grouped_gemm_blockscaled(A, sA, B, sB, group_offsets, out=None):
         raise ValueError("scale grids do not match the operands")
     if tuple(group_offsets.shape) != (E + 1,):
         raise ValueError("group_offsets must have E+1 entries")
+    if out is not None and tuple(out.shape) != (M_total, N):
+        raise ValueError("out has the wrong shape")
     pa = _dev(A, "A", (torch.uint8,))
     psa = _dev(sA, "sA", (torch.float32,))
     pb = _dev(B, "B", (torch.uint8,))
@@ -276,6 +288,8 @@ def fp8_grouped_gemm_wgrad(A, sA, B, sB, group_offsets, M_total, out=None):
         raise ValueError("A and B disagree on the token length")
     if tuple(sA.shape) != (ld // 128, N) or tuple(sB.shape) != (ld // 128, K):
         raise ValueError("scale grids do not match the operands")
+    if out is not None and tuple(out.shape) != (E, N, K):
+        raise ValueError("out has the wrong shape")
     pa = _dev(A, "A", (torch.uint8,))
     psa = _dev(sA, "sA", (torch.float32,))
     pb = _dev(B, "B", (torch.uint8,))
@@ -284,8 +298,6 @@ def fp8_grouped_gemm_wgrad(A, sA, B, sB, group_offsets, M_total, out=None):
     if out is None:
         out = torch.empty((E, N, K), dtype=torch.bfloat16, device=A.device)
     pc = _dev(out, "out", (torch.bfloat16,))
-    if tuple(out.shape) != (E, N, K):
-        raise ValueError("out has the wrong shape")
     _check("fp8_grouped_gemm_wgrad",
            lib().fp8_grouped_gemm_wgrad(pa, psa, pb, psb, pc, po, E, int(M_total), N, K, ld, _stream(A)))
     return out

@@ -1155,6 +1155,17 @@ hipError_t launch_gemm_blockscaled(const uint8_t* A, const float* sA, const uint
   }
 }
 
+void gemm_blockscaled_tile(int64_t M, int64_t N, int64_t K, int row_mode, int* bm, int* bn) {
+  using namespace gemm;
+  (void)K;
+  (void)row_mode;
+  switch (pick_dense(M, N)) {
+    case 1: *bm = Cfg256x224::BM; *bn = Cfg256x224::BN; break;
+    case 2: *bm = Cfg224x256::BM; *bn = Cfg224x256::BN; break;
+    default: *bm = Cfg256x256::BM; *bn = Cfg256x256::BN; break;
+  }
+}
+
 hipError_t launch_gemm_blockscaled_pow2(const uint8_t* A, const float* sA, const uint8_t* B,
                                         const float* sB, int row_mode, uint16_t* C, int64_t M,
                                         int64_t N, int64_t K, hipStream_t stream) {

@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define FP8BS_ABI_VERSION 6
+#define FP8BS_ABI_VERSION 7
 
 #ifndef FP8BS_API
 #define FP8BS_API __attribute__((visibility("default")))
@@ -128,6 +128,17 @@ FP8BS_API int fp8_quant_act_128x1_T(const void* x, int dtype, int64_t M, int64_t
 FP8BS_API int fp8_gemm_blockscaled(const uint8_t* A, const float* sA, const uint8_t* B,
                          const float* sB, int b_scale_mode, uint16_t* C,
                          int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
+ * The output tile fp8_gemm_blockscaled uses for an M x N x K problem in the
+ * given scale mode on the current device: *bm rows by *bn columns per
+ * workgroup (the kernel is chosen per shape so that the tiles fill whole
+ * rounds of the device's compute units). A query only: it launches nothing.
+ * Returns FP8BS_ERR_NULL_PTR if bm or bn is NULL, FP8BS_ERR_MODE for an
+ * unknown mode, FP8BS_ERR_SHAPE for sizes fp8_gemm_blockscaled rejects.
+ */
+FP8BS_API int fp8_gemm_blockscaled_tile(int64_t M, int64_t N, int64_t K, int b_scale_mode,
+                         int* bm, int* bn);
 
 /*
  * Power-of-two scale variant (report section 3.5.2 on the innerforce.co.kr

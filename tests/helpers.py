@@ -98,3 +98,71 @@ def adversarial_rows(n_rows, K, seed=0):
                 v[int(rng.integers(128))] *= 100
             x[r, sl] = np.asarray(v, np.float64).astype(np.float32)
     return x
+
+
+def oracle_threads():
+    """Worker threads for splitting large oracle computations (numpy releases the GIL)."""
+    import os
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def parallel_rows(fn, x, pieces=None):
+    """Apply a row-local oracle function to row blocks of x on a thread pool and
+    return the list of per-block results, in order."""
+    from concurrent.futures import ThreadPoolExecutor
+    n = x.shape[0]
+    pieces = pieces or 4 * oracle_threads()
+    bounds = np.linspace(0, n, pieces + 1).astype(np.int64)
+    blocks = [x[bounds[i]:bounds[i + 1]] for i in range(pieces) if bounds[i + 1] > bounds[i]]
+    with ThreadPoolExecutor(oracle_threads()) as ex:
+        return list(ex.map(fn, blocks))
+
+
+def oracle_quant_act_1x128_big(x):
+    """oracle.quant_act_1x128 of a large [M][K] array, computed in row blocks in
+    parallel (the groups of distinct rows are independent)."""
+    import oracle
+    parts = parallel_rows(oracle.quant_act_1x128, x)
+    return np.concatenate([p[0] for p in parts], axis=0), np.concatenate([p[1] for p in parts], axis=1)
+
+
+def oracle_quant_w_128x128_big(w):
+    """oracle.quant_w_128x128 of a large [N][K] array, by 128-row block bands in parallel."""
+    import oracle
+    from concurrent.futures import ThreadPoolExecutor
+    N = w.shape[0]
+    bands = [w[i:i + 1024] for i in range(0, N, 1024)]
+    with ThreadPoolExecutor(oracle_threads()) as ex:
+        parts = list(ex.map(oracle.quant_w_128x128, bands))
+    return np.concatenate([p[0] for p in parts], axis=0), np.concatenate([p[1] for p in parts], axis=0)
+
+
+def e4m3_encode_parallel(y):
+    """oracle.e4m3_encode of a large 1-D float32 array on a thread pool."""
+    from oracle.e4m3 import e4m3_encode
+    parts = parallel_rows(e4m3_encode, np.asarray(y, np.float32).ravel())
+    return np.concatenate(parts) if parts else np.zeros(0, np.uint8)
+
+
+E4M3_MAX_BITS = int(np.float32(448.0).view(np.uint32))     # 0x43E00000
+
+
+def e4m3_code_thresholds():
+    """T[c-1] = the smallest non-negative float32 bit pattern whose oracle E4M3
+    code is >= c, for c = 1..126, found by bisection with oracle.e4m3_encode.
+
+    The encoder rounds magnitudes to nearest (ties to even) and saturates, so it
+    is monotonic in |x|, and non-negative float32 patterns are ordered as their
+    values: the code of magnitude pattern p <= 448 is searchsorted(T, p, 'right').
+    """
+    from oracle.e4m3 import e4m3_encode
+    lo = np.zeros(126, np.int64)                        # encodes below c
+    hi = np.full(126, E4M3_MAX_BITS, np.int64)          # encodes to >= c
+    target = np.arange(1, 127)
+    while np.any(hi - lo > 1):
+        mid = (lo + hi) // 2
+        c = e4m3_encode(mid.astype(np.uint32).view(np.float32)).astype(np.int64)
+        up = c >= target
+        hi = np.where(up, mid, hi)
+        lo = np.where(up, lo, mid)
+    return hi

@@ -33,7 +33,7 @@ def test_header_declares_the_entry_points():
     names = set(_declared_functions())
     assert {"fp8_quant_act_1x128", "fp8_quant_w_128x128", "fp8_quant_act_128x1_T",
             "fp8_quant_act_128x1_T_grouped", "fp8_gemm_blockscaled", "fp8_gemm_blockscaled_q1x128",
-            "fp8_gemm_blockscaled_q1x128_q128x1T",
+            "fp8_gemm_blockscaled_q1x128_q128x1T", "fp8_gemm_blockscaled_tile",
             "fp8_grouped_gemm_blockscaled", "fp8_grouped_gemm_wgrad", "fp8_moe_dispatch",
             "fp8_moe_dispatch_workspace_bytes", "fp8_moe_combine", "fp8_quant_act_1x128_pow2",
             "fp8_quant_w_128x128_pow2", "fp8_quant_act_128x1_T_pow2", "fp8_gemm_blockscaled_pow2",
@@ -47,7 +47,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.fp8bs_abi_version() == fb.ABI_VERSION == 6
+    assert L.fp8bs_abi_version() == fb.ABI_VERSION == 7
     for code in range(-7, 1):
         assert fb.status_string(code) not in ("", "unknown status")
     assert fb.status_string(-99) == "unknown status"
@@ -180,3 +180,34 @@ def test_binding_requires_gpu_tensors(L):
     x = torch.zeros(4, 128)
     with pytest.raises(ValueError):
         fb.fp8_quant_act_1x128(x)
+
+
+def test_binding_rejects_wrong_output_shapes(L):
+    # the output's shape is checked before anything else touches it, so a
+    # caller-supplied buffer too small for the result is never written
+    import torch
+    u8, f32, bf16 = torch.uint8, torch.float32, torch.bfloat16
+    A = torch.zeros((300, 256), dtype=u8)
+    sA = torch.ones((2, 300), dtype=f32)
+    B = torch.zeros((4, 384, 256), dtype=u8)
+    sB = torch.ones((4, 3, 2), dtype=f32)
+    off = torch.tensor([0, 100, 100, 250, 300], dtype=torch.int32)
+    for bad in ((299, 384), (300, 256), (384, 300)):
+        with pytest.raises(ValueError, match="out has the wrong shape"):
+            fb.fp8_grouped_gemm_blockscaled(A, sA, B, sB, off, out=torch.empty(bad, dtype=bf16))
+    with pytest.raises(ValueError, match="out has the wrong shape"):
+        fb.fp8_gemm_blockscaled(A, sA, B[0], sB[0], out=torch.empty((300, 256), dtype=bf16))
+    qa, sqa = torch.zeros((384, 512), dtype=u8), torch.ones((4, 384), dtype=f32)
+    qb, sqb = torch.zeros((256, 512), dtype=u8), torch.ones((4, 256), dtype=f32)
+    with pytest.raises(ValueError, match="out has the wrong shape"):
+        fb.fp8_grouped_gemm_wgrad(qa, sqa, qb, sqb, off, 300, out=torch.empty((4, 384, 128), dtype=bf16))
+
+
+def test_tile_query_validation(L):
+    import ctypes
+    bm, bn = ctypes.c_int(), ctypes.c_int()
+    q = L.fp8_gemm_blockscaled_tile
+    assert q(4096, 7168, 7168, 2, ctypes.byref(bm), ctypes.byref(bn)) == -5
+    assert q(4096, 7100, 7168, 0, ctypes.byref(bm), ctypes.byref(bn)) == -2
+    assert q(4096, 7168, 7100, 1, ctypes.byref(bm), ctypes.byref(bn)) == -2
+    assert q(4096, 7168, 7168, 0, None, ctypes.byref(bn)) == -1

@@ -140,3 +140,17 @@ def test_encode_rejects_non_finite():
         e4m3_encode(np.array([np.inf], np.float32))
     with pytest.raises(ValueError):
         e4m3_encode(np.array([np.nan], np.float32))
+
+
+def test_code_threshold_table_reproduces_the_encoder():
+    # the table the device converter sweep derives its expected codes from
+    from helpers import E4M3_MAX_BITS, e4m3_code_thresholds, e4m3_encode_parallel
+    T = e4m3_code_thresholds()
+    assert np.all(np.diff(T) > 0)
+    assert T[0] == int(np.float32(2.0 ** -10).view(np.uint32)) + 1   # above half the smallest subnormal
+    near = np.unique(np.clip((T[:, None] + np.arange(-64, 65)[None, :]).ravel(), 0, E4M3_MAX_BITS))
+    stride = np.arange(0, E4M3_MAX_BITS + 1, 4099, dtype=np.int64)
+    p = np.concatenate([near, stride]).astype(np.uint32)
+    want = e4m3_encode_parallel(p.view(np.float32)).astype(np.int64)
+    got = np.searchsorted(T, p.astype(np.int64), side="right")
+    assert np.array_equal(got, want)
