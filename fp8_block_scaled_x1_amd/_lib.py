@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libfp8bs.so")
 
 F32, BF16 = 0, 1
 SCALE_BLOCK128, SCALE_ROW = 0, 1
-ABI_VERSION = 7
+ABI_VERSION = 8
 
 _c_int64 = ctypes.c_int64
 _vp = ctypes.c_void_p
@@ -46,6 +46,8 @@ _SIGNATURES = {
     "fp8_moe_dispatch": [_vp, ctypes.c_int, _c_int64, _c_int64, _vp, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp,
                          _vp, _vp, _vp, _vp],
     "fp8_moe_dispatch_workspace_bytes": [_c_int64, ctypes.c_int, ctypes.c_int],
+    "fp8_moe_dispatch_noalloc": [_vp, ctypes.c_int, _c_int64, _c_int64, _vp, ctypes.c_int, ctypes.c_int, _vp, _vp,
+                                 _vp, _vp, _vp, _vp],
     "fp8_moe_combine": [_vp, _vp, _vp, _c_int64, ctypes.c_int, _c_int64, _vp, _vp],
     "fp8bs_status_string": [ctypes.c_int],
     "fp8bs_abi_version": [],
@@ -330,6 +332,28 @@ def fp8_moe_dispatch(x, topk_ids, E):
            L.fp8_moe_dispatch(px, _in_dtype(x), T, K, pid, topk, E, q.data_ptr(), s.data_ptr(), offsets.data_ptr(),
                               pos.data_ptr(), src.data_ptr(), ws.data_ptr(), _stream(x)))
     return q, s, offsets, pos, src
+
+
+def fp8_moe_dispatch_noalloc(x, topk_ids, E, q, s, offsets, pos, src_row):
+    """fp8_moe_dispatch into caller-provided outputs, with no allocation at all:
+    the routing workspace is the library's own device array (1 MiB per GPU).
+    Shapes as fp8_moe_dispatch returns them; returns the outputs."""
+    if x.dim() != 2 or topk_ids.dim() != 2 or topk_ids.shape[0] != x.shape[0]:
+        raise ValueError("x must be [T][K] and topk_ids [T][topk]")
+    T, K = x.shape
+    topk = topk_ids.shape[1]
+    P = T * topk
+    want = {"q": (P, K), "s": (K // 128 if K % 128 == 0 else 0, P), "offsets": (E + 1,), "pos": (T, topk),
+            "src_row": (P,)}
+    for name, t in (("q", q), ("s", s), ("offsets", offsets), ("pos", pos), ("src_row", src_row)):
+        if tuple(t.shape) != want[name]:
+            raise ValueError(f"{name} has the wrong shape")
+    args = (_dev(x, "x", (torch.float32, torch.bfloat16)), _in_dtype(x), T, K, _dev(topk_ids, "topk_ids", (torch.int32,)),
+            topk, E, _dev(q, "q", (torch.uint8,)), _dev(s, "s", (torch.float32,)),
+            _dev(offsets, "offsets", (torch.int32,)), _dev(pos, "pos", (torch.int32,)),
+            _dev(src_row, "src_row", (torch.int32,)), _stream(x))
+    _check("fp8_moe_dispatch_noalloc", lib().fp8_moe_dispatch_noalloc(*args))
+    return q, s, offsets, pos, src_row
 
 
 def fp8_moe_combine(Y, pos, w):

@@ -92,6 +92,7 @@ const char* fp8bs_status_string(int status) {
     case FP8BS_ERR_MODE: return "unknown scale mode, or transposed outputs given one-sided";
     case FP8BS_ERR_LAUNCH: return "kernel launch failed";
     case FP8BS_ERR_TOO_LARGE: return "size exceeds the supported 32-bit index range";
+    case FP8BS_ERR_SCRATCH: return "the problem needs more scratch memory than the no-allocation entry point holds";
     default: return "unknown status";
   }
 }
@@ -228,6 +229,39 @@ int64_t fp8_moe_dispatch_workspace_bytes(int64_t T, int topk, int E) {
   if (T < 0 || topk < 1 || topk > 64 || E < 1 || E > fp8bs::moe_max_experts()) return FP8BS_ERR_SHAPE;
   if (T * topk >= kI32) return FP8BS_ERR_TOO_LARGE;
   return 4 * (int64_t)E * fp8bs::moe_route_blocks(T * topk);
+}
+
+namespace {
+// argument checks shared by both dispatch entry points (workspace aside)
+int dispatch_checks(const void* x, int dtype, int64_t T, int64_t K, const int32_t* topk_ids, int topk, int E,
+                    uint8_t* q, float* s, int32_t* offsets, int32_t* pos, int32_t* src_row) {
+  if (!valid_dtype(dtype)) return FP8BS_ERR_DTYPE;
+  if (T < 0 || K < 0 || K % kG || topk < 1 || topk > 64 || E < 1 || E > fp8bs::moe_max_experts())
+    return FP8BS_ERR_SHAPE;
+  const int64_t P = T * topk;
+  if (P >= kI32 || K >= kI32 || (K / kG + 3) / 4 > 65535 || (T + 7) / 8 >= (int64_t)1 << 27)
+    return FP8BS_ERR_TOO_LARGE;
+  if (!offsets) return FP8BS_ERR_NULL_PTR;
+  if (P > 0 && (!topk_ids || !pos || !src_row)) return FP8BS_ERR_NULL_PTR;
+  if (P > 0 && K > 0 && (!x || !q || !s)) return FP8BS_ERR_NULL_PTR;
+  if (misaligned(x) || misaligned(q) || misaligned(s)) return FP8BS_ERR_ALIGN;
+  auto mis4 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) != 0; };
+  if (mis4(topk_ids) || mis4(offsets) || mis4(pos) || mis4(src_row)) return FP8BS_ERR_ALIGN;
+  return FP8BS_OK;
+}
+}  // namespace
+
+int fp8_moe_dispatch_noalloc(const void* x, int dtype, int64_t T, int64_t K, const int32_t* topk_ids, int topk,
+                             int E, uint8_t* q, float* s, int32_t* offsets, int32_t* pos, int32_t* src_row,
+                             void* stream) {
+  const int st = dispatch_checks(x, dtype, T, K, topk_ids, topk, E, q, s, offsets, pos, src_row);
+  if (st != FP8BS_OK) return st;
+  if (4 * (int64_t)E * fp8bs::moe_route_blocks(T * topk) > fp8bs::kMoeScratchBytes) return FP8BS_ERR_SCRATCH;
+  int32_t* ws = nullptr;
+  const hipError_t e = fp8bs::moe_scratch(as_stream(stream), &ws);
+  if (e != hipSuccess) return FP8BS_ERR_LAUNCH;
+  return status_of(fp8bs::launch_moe_dispatch(x, dtype == FP8BS_BF16, T, K, topk_ids, topk, E, q, s, offsets,
+                                              pos, src_row, ws, as_stream(stream)));
 }
 
 int fp8_moe_dispatch(const void* x, int dtype, int64_t T, int64_t K, const int32_t* topk_ids, int topk, int E,

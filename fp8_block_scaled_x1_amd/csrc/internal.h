@@ -43,6 +43,10 @@ hipError_t launch_grouped_gemm_blockscaled(const uint8_t* A, const float* sA, co
                                            hipStream_t stream);
 
 int64_t moe_route_blocks(int64_t pairs);
+// the no-allocation dispatch's routing workspace: a device array of this many
+// bytes per GPU; moe_scratch gives its device address on the stream's GPU
+constexpr int64_t kMoeScratchBytes = (int64_t)1 << 20;
+hipError_t moe_scratch(hipStream_t stream, int32_t** ptr);
 int moe_max_experts();
 hipError_t launch_moe_dispatch(const void* x, bool bf16, int64_t T, int64_t K, const int32_t* ids, int topk,
                                int E, uint8_t* q, float* s, int32_t* offsets, int32_t* pos, int32_t* src,

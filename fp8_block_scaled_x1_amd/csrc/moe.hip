@@ -19,6 +19,8 @@
 //   combine:   out[t] = bf16( sum_j w[t][j] * Y[pos[t][j]] ), FP32 sums in
 //              slot order.
 
+#include <mutex>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -375,5 +377,47 @@ hipError_t launch_moe_combine(const uint16_t* Y, const int32_t* pos, const float
 }
 
 int moe_max_experts() { return kMaxExperts; }
+
+// ---------------------------------------------------------------------------
+// Scratch memory of the no-allocation dispatch entry point: the routing
+// workspace lives in this file-scope device array (each GPU the library runs
+// on holds its own copy until the process ends) instead of caller memory.
+// Host code never uses the array's name as an address: the device address of
+// each GPU's copy is looked up once per device, with that device current,
+// and kept.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) int32_t scratch[kMoeScratchBytes / 4];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+int32_t* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t moe_scratch(hipStream_t stream, int32_t** ptr) {
+  int cur = 0, dev = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return e;
+  dev = cur;
+  if (stream != nullptr) {
+    e = hipStreamGetDevice(stream, &dev);
+    if (e != hipSuccess) return e;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = static_cast<int32_t*>(p);
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 }  // namespace fp8bs

@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define FP8BS_ABI_VERSION 7
+#define FP8BS_ABI_VERSION 8
 
 #ifndef FP8BS_API
 #define FP8BS_API __attribute__((visibility("default")))
@@ -65,7 +65,9 @@ enum fp8bs_status {
   FP8BS_ERR_DTYPE = -4,    /* unknown dtype                                   */
   FP8BS_ERR_MODE = -5,     /* unknown scale mode, or qT/sT given one-sided    */
   FP8BS_ERR_LAUNCH = -6,   /* the HIP runtime rejected a kernel launch        */
-  FP8BS_ERR_TOO_LARGE = -7 /* a size exceeds the 32-bit index range supported */
+  FP8BS_ERR_TOO_LARGE = -7, /* a size exceeds the 32-bit index range supported */
+  FP8BS_ERR_SCRATCH = -8    /* more scratch memory needed than a no-allocation
+                               entry point holds                             */
 };
 
 /*
@@ -295,6 +297,24 @@ FP8BS_API int fp8_moe_dispatch(const void* x, int dtype, int64_t T, int64_t K,
 
 /* Workspace bytes fp8_moe_dispatch needs (negative: invalid sizes). */
 FP8BS_API int64_t fp8_moe_dispatch_workspace_bytes(int64_t T, int topk, int E);
+
+/*
+ * fp8_moe_dispatch for callers that cannot allocate memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same routing, payload and outputs, bit for bit, without the workspace
+ * argument. The routing workspace is a device array inside the library, 1 MiB
+ * on each GPU it runs on, held until the process ends; the call allocates
+ * nothing. Problems whose workspace (fp8_moe_dispatch_workspace_bytes) exceeds
+ * 1 MiB, i.e. 4 * E * ceil(T*topk / 1024) > 2^20, return FP8BS_ERR_SCRATCH
+ * before anything is enqueued. Every call on one GPU uses that GPU's array:
+ * calls that may run at the same time on one GPU (on different streams) race
+ * and must be ordered by the caller. Other arguments, layouts and errors as
+ * for fp8_moe_dispatch.
+ */
+FP8BS_API int fp8_moe_dispatch_noalloc(const void* x, int dtype, int64_t T, int64_t K,
+                          const int32_t* topk_ids, int topk, int E,
+                          uint8_t* q, float* s, int32_t* offsets, int32_t* pos,
+                          int32_t* src_row, void* stream);
 
 /*
  * MoE combine in BF16 (report section 3.3.3: the combine is kept in BF16,

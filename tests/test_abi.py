@@ -35,7 +35,7 @@ def test_header_declares_the_entry_points():
             "fp8_quant_act_128x1_T_grouped", "fp8_gemm_blockscaled", "fp8_gemm_blockscaled_q1x128",
             "fp8_gemm_blockscaled_q1x128_q128x1T", "fp8_gemm_blockscaled_tile",
             "fp8_grouped_gemm_blockscaled", "fp8_grouped_gemm_wgrad", "fp8_moe_dispatch",
-            "fp8_moe_dispatch_workspace_bytes", "fp8_moe_combine", "fp8_quant_act_1x128_pow2",
+            "fp8_moe_dispatch_workspace_bytes", "fp8_moe_dispatch_noalloc", "fp8_moe_combine", "fp8_quant_act_1x128_pow2",
             "fp8_quant_w_128x128_pow2", "fp8_quant_act_128x1_T_pow2", "fp8_gemm_blockscaled_pow2",
             "fp8bs_status_string", "fp8bs_abi_version"} == names
 
@@ -47,8 +47,8 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.fp8bs_abi_version() == fb.ABI_VERSION == 7
-    for code in range(-7, 1):
+    assert L.fp8bs_abi_version() == fb.ABI_VERSION == 8
+    for code in range(-8, 1):
         assert fb.status_string(code) not in ("", "unknown status")
     assert fb.status_string(-99) == "unknown status"
 
@@ -211,3 +211,17 @@ def test_tile_query_validation(L):
     assert q(4096, 7100, 7168, 0, ctypes.byref(bm), ctypes.byref(bn)) == -2
     assert q(4096, 7168, 7100, 1, ctypes.byref(bm), ctypes.byref(bn)) == -2
     assert q(4096, 7168, 7168, 0, None, ctypes.byref(bn)) == -1
+
+
+def test_noalloc_dispatch_validation(L):
+    # rejected on the host, before any device call: invalid sizes, and a
+    # routing workspace beyond the library's 1 MiB scratch array
+    d = L.fp8_moe_dispatch_noalloc
+    assert d(P, 1, 16, 128, P, 0, 8, P, P, P, P, P, NULL) == -2                  # topk < 1
+    assert d(P, 1, 16, 100, P, 2, 8, P, P, P, P, P, NULL) == -2                  # K % 128
+    assert d(P, 3, 16, 128, P, 2, 8, P, P, P, P, P, NULL) == -4
+    assert d(P, 1, 16, 128, P, 2, 8, P, P, NULL, P, P, NULL) == -1
+    assert d(MIS, 1, 16, 128, P, 2, 8, P, P, P, P, P, NULL) == -3
+    # E * ceil(T*topk/1024) * 4 bytes: 1024 experts x 257 blocks > 2^20
+    assert d(P, 1, 257 * 128, 128, P, 8, 1024, P, P, P, P, P, NULL) == -8
+    assert fb.status_string(-8).startswith("the problem needs more scratch memory")
