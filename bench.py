@@ -126,18 +126,66 @@ class Timer:
             self.k = 0
             self.i += 1
 
-    def averages_us(self):
+    def samples_us(self):
         out = {}
         for j, n in enumerate(self.names):
-            ts = [self.events.elapsed_ms(row[j], row[j + 1]) * 1e3 for row in self.ev[:self.i]]
-            out[n] = sum(ts) / len(ts)
+            out[n] = [self.events.elapsed_ms(row[j], row[j + 1]) * 1e3 for row in self.ev[:self.i]]
         return out
+
+    def averages_us(self):
+        return {n: sum(ts) / len(ts) for n, ts in self.samples_us().items()}
 
     def close(self):
         for row in self.ev:
             for e in row:
                 self.events.destroy(e)
         self.ev = []
+
+
+class ClockSampler:
+    """Samples the GPU's current shader clock (amdsmi, through torch) every
+    few milliseconds on a background thread while the timed steps run."""
+
+    def __init__(self, torch, period_s=0.005):
+        import threading
+        self.torch = torch
+        self.period = period_s
+        self.samples = []
+        self.stop_evt = threading.Event()
+        self.thread = threading.Thread(target=self._run, daemon=True)
+
+    def _run(self):
+        while not self.stop_evt.is_set():
+            try:
+                mhz = float(self.torch.cuda.clock_rate(0))
+            except Exception:
+                return
+            if mhz > 0:
+                self.samples.append(mhz)
+            self.stop_evt.wait(self.period)
+
+    def __enter__(self):
+        self.thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self.stop_evt.set()
+        self.thread.join()
+
+    def summary(self):
+        if not self.samples:
+            return None
+        xs = sorted(self.samples)
+        return {"median_mhz": xs[len(xs) // 2], "min_mhz": xs[0], "max_mhz": xs[-1], "samples": len(xs)}
+
+
+def percentile(xs, q):
+    xs = sorted(xs)
+    if not xs:
+        return float("nan")
+    k = (len(xs) - 1) * q
+    lo, hi = int(k), min(int(k) + 1, len(xs) - 1)
+    return xs[lo] + (xs[hi] - xs[lo]) * (k - lo)
 
 
 # ---------------------------------------------------------------------------
@@ -227,6 +275,46 @@ def setup_dense_fprop(torch, fb, dev, M=4096, N=7168, K=7168, fused=False, pow2=
         "dominant": gemm,
         "config": {"workload": f"dense Fprop projection X[{M}x{K}] bf16 1x128, W[{N}x{K}] bf16 128x128, "
                                f"{out}", "M": M, "N": N, "K": K, "input_rotations": R},
+    }
+    return step, info
+
+
+def setup_tiny_fprop(torch, fb, dev, M=256, N=512, K=1024):
+    """The tiny Fprop: X[256x1024] and W[512x1024] float32 quantized 1x128 and
+    128x128, then the GEMM (launch-latency bound; reported in microseconds)."""
+    import workloads
+    d = workloads.tiny_fprop(device=dev, M=M, N=N, K=K)
+    X, W = d["X"], d["W"]
+    qx = torch.empty((M, K), dtype=torch.uint8, device=dev)
+    sx = torch.empty((K // 128, M), dtype=torch.float32, device=dev)
+    qw = torch.empty((N, K), dtype=torch.uint8, device=dev)
+    sw = torch.empty((N // 128, K // 128), dtype=torch.float32, device=dev)
+    C = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    L = fb.lib()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+
+    def step(timer):
+        timer.mark()
+        rc = L.fp8_quant_act_1x128(X.data_ptr(), fb.F32, M, K, qx.data_ptr(), sx.data_ptr(), stream)
+        timer.mark()
+        rc |= L.fp8_quant_w_128x128(W.data_ptr(), fb.F32, N, K, qw.data_ptr(), sw.data_ptr(), None, None, stream)
+        timer.mark()
+        rc |= L.fp8_gemm_blockscaled(qx.data_ptr(), sx.data_ptr(), qw.data_ptr(), sw.data_ptr(), fb.SCALE_BLOCK128,
+                                     C.data_ptr(), M, N, K, stream)
+        timer.mark()
+        if rc:
+            raise RuntimeError(f"libfp8bs call failed ({rc})")
+
+    flops = 2.0 * M * N * K
+    info = {
+        "names": ["quant_act_1x128", "quant_w_128x128", "gemm_blockscaled"],
+        "step_flops": flops,
+        "work": {"quant_act_1x128": ("GB/s", M * K * 4 + M * K + M * K // 128 * 4),
+                 "quant_w_128x128": ("GB/s", N * K * 4 + N * K + N * K // 16384 * 4),
+                 "gemm_blockscaled": ("TFLOP/s", flops)},
+        "dominant": "gemm_blockscaled",
+        "config": {"workload": f"tiny Fprop X[{M}x{K}] f32 1x128, W[{N}x{K}] f32 128x128, C[{M}x{N}] bf16 "
+                               f"(launch-latency bound)", "M": M, "N": N, "K": K},
     }
     return step, info
 
@@ -556,7 +644,8 @@ def setup_copy(torch, fb, dev, nbytes=None):
     return step, info
 
 
-WORKLOADS = {"copy": setup_copy, "dense_fprop": setup_dense_fprop, "fprop_q1x128": setup_fprop_q1x128,
+WORKLOADS = {"copy": setup_copy, "tiny_fprop": setup_tiny_fprop, "dense_fprop": setup_dense_fprop,
+             "fprop_q1x128": setup_fprop_q1x128,
              "fprop_pow2": setup_fprop_pow2, "fprop_qboth": setup_fprop_qboth,
              "backward": setup_backward, "moe": setup_moe, "moe_backward": setup_moe_backward,
              "moe_dispatch": setup_moe_dispatch, "decode": setup_decode}
@@ -639,6 +728,86 @@ def cpu_baseline(workload):
             "sample": f"one Fprop step at {M}x{N}x{K}: quantize X 1x128 and W 128x128, {what}; {dt:.1f} s"}
 
 
+def run_workload(torch, fb, dev, name, steps, warmup, ramp_ms, clock_ms=300.0):
+    """Set up one workload, ramp the clocks, warm up, time `steps` steps.
+
+    Returns the step function's info, the wall-clock ms per step, per-kernel
+    statistics (HIP events on the launch stream, one pair per kernel and
+    step) and the shader clock sampled while the same steps run on after the
+    timed ones."""
+    step, info = WORKLOADS[name](torch, fb, dev)
+    names = info["names"]
+    events = HipTimingEvents(torch)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    warm = Timer(torch, names, 0, stream, events)
+    # The MI355X raises its clocks over the first ~100 ms under load: a few
+    # warm-up steps alone leave the timed steps at ramp-up clocks (the dense
+    # GEMM measured 15% slower). Untimed steps for ramp_ms come first.
+    ramp_steps, t_ramp = 0, time.perf_counter()
+    while (time.perf_counter() - t_ramp) * 1e3 < ramp_ms and ramp_steps < 20000:
+        for _ in range(4):
+            step(warm)
+        ramp_steps += 4
+        torch.cuda.synchronize()
+    ramp = {"steps": ramp_steps, "ms": round((time.perf_counter() - t_ramp) * 1e3, 1)}
+    for _ in range(warmup):
+        step(warm)
+    torch.cuda.synchronize()
+    timer = Timer(torch, names, steps, stream, events)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step(timer)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / steps
+    samples = timer.samples_us()
+    timer.close()
+    # The shader clock under this workload's load: the same steps, untimed, for
+    # clock_ms more while the clock is sampled (the sampled value is an average
+    # over the sensor's own period, so the window is longer than that period).
+    try:
+        torch.cuda.clock_rate(0)        # initializes the query before the window
+    except Exception:
+        pass
+    with ClockSampler(torch) as clk:
+        t_c = time.perf_counter()
+        while (time.perf_counter() - t_c) * 1e3 < clock_ms:
+            for _ in range(4):
+                step(warm)
+            torch.cuda.synchronize()
+    kernels = {}
+    for n in names:
+        unit, work = info["work"][n]
+        ts = samples[n]
+        mean = sum(ts) / len(ts)
+        scale = 1e12 if unit == "TFLOP/s" else 1e9
+        peak = PEAK_FP8_TFLOPS if unit == "TFLOP/s" else PEAK_HBM_GBS
+        rate = work / (mean * 1e-6) / scale
+        kernels[n] = {"us": round(mean, 2), "us_median": round(percentile(ts, 0.5), 2),
+                      "us_p10": round(percentile(ts, 0.1), 2), "us_p90": round(percentile(ts, 0.9), 2),
+                      unit: round(rate, 1), "frac_of_peak": round(rate / peak, 4)}
+    del step
+    return info, ms_per_step, kernels, clk.summary(), ramp
+
+
+def device_summary(torch, dev, clock):
+    props = torch.cuda.get_device_properties(dev)
+    cus = props.multi_processor_count
+    out = {"name": props.name, "compute_units": cus}
+    if clock:
+        mhz = clock["median_mhz"]
+        out["sclk_mhz_under_load"] = clock
+        out["fp8_peak_at_that_sclk_tflops"] = round(cus * 8192 * mhz * 1e6 / 1e12, 1)
+    return out
+
+
+# Sub-results measured by the default run besides the headline: every
+# workload configuration of the benchmark definition, each its own short run.
+EXTRA_CONFIGS = [("1_tiny_fprop", "tiny_fprop"), ("3_moe_grouped", "moe"), ("4_decode_grouped", "decode"),
+                 ("5_backward_pair", "backward")]
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -646,6 +815,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", choices=sorted(WORKLOADS), default="dense_fprop")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="with the default workload, skip the sub-results of the other configurations")
+    ap.add_argument("--config-steps", type=int, default=20, help="timed steps of each other configuration")
     ap.add_argument("--clock-ramp-ms", type=float, default=300.0,
                     help="untimed steps for this long before the warm-up steps, so that the GPU clocks "
                          "reach their loaded steady state (0 to skip)")
@@ -663,49 +835,15 @@ def main():
         sys.exit(1)
     fb.lib()   # fails loudly if the HIP library is missing
     dev = torch.device("cuda:0")
-    step, info = WORKLOADS[args.workload](torch, fb, dev)
-    names = info["names"]
-
-    events = HipTimingEvents(torch)
-    stream = torch.cuda.current_stream(dev).cuda_stream
-    warm = Timer(torch, names, 0, stream, events)
-    # The MI355X raises its clocks over the first ~100 ms under load: a few
-    # warm-up steps alone leave the timed steps at ramp-up clocks (the dense
-    # GEMM measured 15% slower). Untimed steps for --clock-ramp-ms come first.
-    ramp_steps, t_ramp = 0, time.perf_counter()
-    while (time.perf_counter() - t_ramp) * 1e3 < args.clock_ramp_ms and ramp_steps < 20000:
-        for _ in range(4):
-            step(warm)
-        ramp_steps += 4
-        torch.cuda.synchronize()
-    ramp_ms = (time.perf_counter() - t_ramp) * 1e3
-    for _ in range(args.warmup):
-        step(warm)
-    torch.cuda.synchronize()
-    timer = Timer(torch, names, args.steps, stream, events)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step(timer)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-
-    per_kernel = timer.averages_us()
-    timer.close()
-    kernels = {}
-    for n in names:
-        unit, work = info["work"][n]
-        us = per_kernel[n]
-        rate = work / (us * 1e-6) / (1e12 if unit == "TFLOP/s" else 1e9)
-        peak = PEAK_FP8_TFLOPS if unit == "TFLOP/s" else PEAK_HBM_GBS
-        kernels[n] = {"us": round(us, 2), unit: round(rate, 1), "frac_of_peak": round(rate / peak, 4)}
+    info, ms_per_step, kernels, clock, ramp = run_workload(torch, fb, dev, args.workload, args.steps, args.warmup,
+                                                           args.clock_ramp_ms)
+    torch.cuda.empty_cache()
 
     dom = info["dominant"]
     unit, work = info["work"][dom]
-    achieved = work / (per_kernel[dom] * 1e-6) / (1e12 if unit == "TFLOP/s" else 1e9)
+    achieved = kernels[dom][unit]
     peak = PEAK_FP8_TFLOPS if unit == "TFLOP/s" else PEAK_HBM_GBS
-    roofline = {"bound": "mfma" if unit == "TFLOP/s" else "hbm", "achieved": round(achieved, 1), "peak": peak,
+    roofline = {"bound": "mfma" if unit == "TFLOP/s" else "hbm", "achieved": achieved, "peak": peak,
                 "unit": unit, "frac": round(achieved / peak, 4),
                 "traffic": measured_traffic(dom, args.workload), "kernel": dom,
                 "work_per_launch": work}
@@ -720,8 +858,16 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3 (fp32 accumulate, bf16 out)",
         "data": "synthetic (seeded; shapes and distributions of the workload)",
         "config": info["config"], "kernels": kernels, "roofline": roofline,
-        "clock_ramp": {"steps": ramp_steps, "ms": round(ramp_ms, 1)},
+        "device": device_summary(torch, dev, clock), "clock_ramp": ramp,
     }
+    if args.workload == "dense_fprop" and not args.no_configs:
+        configs = {}
+        for key, wl in EXTRA_CONFIGS:
+            cinfo, cms, ck, cclk, _ = run_workload(torch, fb, dev, wl, args.config_steps, 3, 100.0)
+            configs[key] = {"workload": cinfo["config"]["workload"], "ms_per_step": round(cms, 4),
+                            "kernels": ck, "sclk_median_mhz": cclk["median_mhz"] if cclk else None}
+            torch.cuda.empty_cache()
+        line["configs"] = configs
     if not args.no_cpu_baseline and args.workload != "copy":
         line["cpu_baseline"] = cpu_baseline(args.workload)
     print(json.dumps(line), flush=True)

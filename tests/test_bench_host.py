@@ -44,3 +44,18 @@ def test_committed_traffic_table_is_well_formed():
         assert workload in bench.WORKLOADS
         assert abs(ent["bytes_per_launch"] - ent["fetch_bytes"] - ent["write_bytes"]) <= 1   # each rounded
         assert len(ent["source_digest"]) == 16
+
+
+def test_percentile_interpolates():
+    xs = [4.0, 1.0, 3.0, 2.0]
+    assert bench.percentile(xs, 0.0) == 1.0 and bench.percentile(xs, 1.0) == 4.0
+    assert bench.percentile(xs, 0.5) == 2.5
+    assert abs(bench.percentile(list(range(11)), 0.1) - 1.0) < 1e-12
+
+
+def test_default_run_covers_every_configuration():
+    # the headline is the dense Fprop; the default run adds the tiny Fprop,
+    # the grouped MoE GEMMs, the decode-shaped grouped GEMM and the backward pair
+    names = [wl for _, wl in bench.EXTRA_CONFIGS]
+    assert names == ["tiny_fprop", "moe", "decode", "backward"]
+    assert all(wl in bench.WORKLOADS for wl in names)
