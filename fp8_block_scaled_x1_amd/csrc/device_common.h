@@ -278,8 +278,8 @@ __device__ __forceinline__ uint32_t pack4(uint32_t c0, uint32_t c1, uint32_t c2,
 // ---------------------------------------------------------------------------
 // Per-expert work lists. Expert e owns rows [a_e, b_e) with
 // a_e = clamp(off[e], 0, M_total) and b_e = clamp(off[e+1], a_e, M_total);
-// it has units(e) = ceil((b_e - a_e) / unit_rows) * mult work units, numbered
-// expert-major. Lane l of the calling wave examines expert e0 + l of each
+// it has units(e) = ceil((b_e - a_e) / unit_rows) * mult work units (none if
+// it has min_rows rows or fewer), numbered expert-major. Lane l of the calling wave examines expert e0 + l of each
 // batch of 64 (the offsets of a batch are read at once) and a prefix sum over
 // the lanes finds the answer; every result is wave-uniform.
 // ---------------------------------------------------------------------------
@@ -290,7 +290,7 @@ struct ExpertSlot {
 };
 
 __device__ __forceinline__ ExpertSlot locate_expert(const int32_t* __restrict__ off, int E, int M_total,
-                                                    int unit, int unit_rows, int mult) {
+                                                    int unit, int unit_rows, int mult, int min_rows = 0) {
   const int lane = threadIdx.x & 63;
   ExpertSlot r{-1, 0, 0, 0};
   int base = 0;
@@ -300,7 +300,7 @@ __device__ __forceinline__ ExpertSlot locate_expert(const int32_t* __restrict__ 
     if (e < E) {
       a = min(max(off[e], 0), M_total);
       b = min(max(off[e + 1], a), M_total);
-      ue = ((b - a + unit_rows - 1) / unit_rows) * mult;
+      ue = b - a > min_rows ? ((b - a + unit_rows - 1) / unit_rows) * mult : 0;
     }
     int incl = ue;
 #pragma unroll

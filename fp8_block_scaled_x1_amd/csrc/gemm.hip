@@ -787,18 +787,19 @@ __global__ __launch_bounds__(G::kThreads, 1) void gemm_kernel(const uint8_t* __r
 }
 
 // Per-expert tiles: expert e owns rows [off[e], off[e+1]); its tiles are
-// ceil(rows/BM) x ceil(N/BN), numbered expert-major. The grid is an upper
-// bound on the total; workgroups past the last tile exit at once.
+// ceil(rows/BM) x ceil(N/BN), numbered expert-major; experts with min_rows
+// rows or fewer have none (the decode kernel takes them). The grid is an
+// upper bound on the total; workgroups past the last tile exit at once.
 template <class G>
 __global__ __launch_bounds__(G::kThreads, 1) void grouped_gemm_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ sA, const uint8_t* __restrict__ B,
     const float* __restrict__ sB, uint16_t* __restrict__ C, const int32_t* __restrict__ offsets,
-    int E, int M_total, int N, int K) {
+    int E, int M_total, int N, int K, int min_rows) {
   __shared__ __align__(16) uint8_t smem[G::kLdsBytes];
   const int tiles_n = (N + G::BN - 1) / G::BN;
   const int pid = xcd_remap(blockIdx.x, gridDim.x);
   // the expert of tile pid (tiles numbered expert-major)
-  const ExpertSlot es = locate_expert(offsets, E, M_total, pid, G::BM, tiles_n);
+  const ExpertSlot es = locate_expert(offsets, E, M_total, pid, G::BM, tiles_n, min_rows);
   if (es.e < 0) return;
   const int e_found = es.e, r0 = es.r0, r1 = es.r1, base = es.base;
   int tm, tn;
@@ -1075,10 +1076,11 @@ __device__ __forceinline__ void run_pass(const Pass a, uint8_t* smem) {
 }
 }  // namespace dec
 
+// Experts with more than max_rows rows are left to the tile kernel.
 __global__ __launch_bounds__(dec::kThreads, 1) void grouped_decode_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ sA, const uint8_t* __restrict__ B,
     const float* __restrict__ sB, uint16_t* __restrict__ C, const int32_t* __restrict__ offsets, int E,
-    int M_total, int N, int K) {
+    int M_total, int N, int K, int max_rows) {
   __shared__ __align__(16) uint8_t smem[dec::kLds];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1118,7 +1120,7 @@ __global__ __launch_bounds__(dec::kThreads, 1) void grouped_decode_kernel(
   }
   int r0, r1;
   rows_of(e, r0, r1);
-  if (r1 <= r0) return;                            // no rows: nothing to write
+  if (r1 <= r0 || r1 - r0 > max_rows) return;     // no rows, or the tile kernel's expert
   dec::Pass a;
   a.A = A; a.sA = sA; a.C = C; a.M_total = M_total; a.N = N; a.K = K; a.nkb = K / BK;
   a.n_col0 = nb * dec::kBN;
@@ -1203,23 +1205,33 @@ hipError_t launch_grouped_gemm_blockscaled(const uint8_t* A, const float* sA, co
                                            int E, int64_t M_total, int64_t N, int64_t K,
                                            hipStream_t stream) {
   using namespace gemm;
-  // every expert adds at most one partial m-tile beyond M_total / BM
-  auto launch = [&](auto cfg) {
-    using G = decltype(cfg);
-    const int64_t tiles = ((M_total + G::BM - 1) / G::BM + E) * ((N + G::BN - 1) / G::BN);
-    hipLaunchKernelGGL((grouped_gemm_kernel<G>), dim3((unsigned)tiles), dim3(G::kThreads), 0, stream, A,
-                       sA, B, sB, C, offsets, E, (int)M_total, (int)N, (int)K);
-    return hipGetLastError();
-  };
-  // Few rows per expert on average (decode): the weight-streaming kernel,
-  // which reads every expert's weights once whatever its rows
-  if (M_total < (int64_t)E * 256) {
-    const int64_t blocks = (int64_t)E * ((N + dec::kBN - 1) / dec::kBN);
-    hipLaunchKernelGGL(grouped_decode_kernel, dim3((unsigned)blocks), dim3(dec::kThreads), 0, stream, A, sA, B, sB,
-                       C, offsets, E, (int)M_total, (int)N, (int)K);
+  using G = Cfg256x256;
+  const int64_t tiles_n = (N + G::BN - 1) / G::BN;
+  // Many rows per expert on average: the tile kernel for every expert; every
+  // expert adds at most one partial m-tile beyond M_total / BM.
+  if (M_total >= (int64_t)E * dec::kBM) {
+    const int64_t tiles = ((M_total + G::BM - 1) / G::BM + E) * tiles_n;
+    hipLaunchKernelGGL((grouped_gemm_kernel<G>), dim3((unsigned)tiles), dim3(G::kThreads), 0, stream, A, sA, B,
+                       sB, C, offsets, E, (int)M_total, (int)N, (int)K, 0);
     return hipGetLastError();
   }
-  return launch(Cfg256x256{});
+  // Few rows per expert on average (decode): the weight-streaming kernel for
+  // experts of at most one 256-row pass, which reads their weights once
+  // whatever their rows; the offsets live on the device, so any expert with
+  // more rows (a skewed batch) is left to the tile kernel, launched behind it
+  // for those experts only: at most M_total / 257 of them, adding at most
+  // one partial m-tile each.
+  const int64_t blocks = (int64_t)E * ((N + dec::kBN - 1) / dec::kBN);
+  hipLaunchKernelGGL(grouped_decode_kernel, dim3((unsigned)blocks), dim3(dec::kThreads), 0, stream, A, sA, B, sB,
+                     C, offsets, E, (int)M_total, (int)N, (int)K, dec::kBM);
+  const int64_t big = M_total / (dec::kBM + 1);
+  if (big == 0) return hipGetLastError();
+  const hipError_t e1 = hipGetLastError();
+  if (e1 != hipSuccess) return e1;
+  const int64_t tiles = ((M_total + G::BM - 1) / G::BM + big) * tiles_n;
+  hipLaunchKernelGGL((grouped_gemm_kernel<G>), dim3((unsigned)tiles), dim3(G::kThreads), 0, stream, A, sA, B, sB,
+                     C, offsets, E, (int)M_total, (int)N, (int)K, dec::kBM);
+  return hipGetLastError();
 }
 
 hipError_t launch_grouped_gemm_wgrad(const uint8_t* A, const float* sA, const uint8_t* B,

@@ -7,7 +7,9 @@
   one full output row per m-tile, the row's offset inside its tile moving
   from tile to tile, so every wave row and both halves of every tile are seen.
 * The grouped GEMM's tile kernel (chosen when the experts average 256 rows or
-  more) on ragged experts that include empty ones.
+  more) on ragged experts that include empty ones, and skewed batches whose
+  few large experts go to the tile kernel while the rest take the
+  weight-streaming kernel.
 * The MoE activation and expert-weight quantizers at their full sizes
   (65,536 x 7,168 and 65,536 x 2,048 activations, 32 x 4,096 x 7,168 and
   32 x 7,168 x 2,048 weights), bit for bit against the oracle.
@@ -169,3 +171,26 @@ def test_moe_expert_weight_quantizers_full_size(dev):
             assert_codes_equal(u8(q), qo, f"{key}[{e}] codes")
             assert_scales_equal(s.cpu().numpy(), so, f"{key}[{e}] scales")
         del W
+
+
+@pytest.mark.parametrize("counts,N,K", [
+    ([3000] + [int(c) for c in np.random.default_rng(9).integers(1, 21, 31)], 512, 768),   # one big among tiny
+    ([5, 600, 3, 0, 300, 1], 384, 512),                         # two experts past one 256-row pass
+    ([257, 0, 256, 1], 256, 256),                               # at the 256-row boundary
+])
+def test_grouped_skewed_experts_take_both_kernels(dev, counts, N, K):
+    # few rows per expert on average, so the weight-streaming kernel runs, but
+    # the experts with more than 256 rows go to the tile kernel
+    off = np.zeros(len(counts) + 1, np.int32)
+    off[1:] = np.cumsum(counts)
+    M, E = int(off[-1]), len(counts)
+    assert M < 256 * E and max(counts) > 256
+    seed = 3 * M + N
+    A, sA = _codes((M, K), seed), _scales((K // 128, M), seed + 1)
+    B, sB = _codes((E, N, K), seed + 2), _scales((E, N // 128, K // 128), seed + 3)
+    C = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=dev)
+    fb.fp8_grouped_gemm_blockscaled(A.to(dev), sA.to(dev), B.to(dev), sB.to(dev), torch.from_numpy(off).to(dev),
+                                    out=C)
+    ref, absref = oracle.grouped_gemm_ref(A.numpy(), sA.numpy(), B.numpy(), sB.numpy(), off)
+    torch.cuda.synchronize()
+    _check(C, ref, absref, f"grouped skewed {counts[:4]}... N={N} K={K}")
