@@ -593,10 +593,18 @@ __device__ __forceinline__ void run_tile(const Tile& t, uint8_t* smem) {
     }
   }
 
-  // lane holds C[m][n..n+3] of every MFMA tile
-  const int m_lane = t.m0 + wm * WM + (lane & 15);
-  const int n_lane = t.n0 + wn * WN + 4 * (lane >> 4);
-  const int r_lane = wm * WM + (lane & 15), c_lane = wn * WN + 4 * (lane >> 4);   // the same within the tile
+  // lane holds C[m][n..n+3] of every MFMA tile. With the accumulators in
+  // AGPRs (HW) the lane index is read again here rather than kept in a VGPR
+  // through the main loop, where every VGPR is taken.
+  int lane_e = lane;
+  if constexpr (HW) {
+    lane_e = (int)threadIdx.x;
+    asm volatile("" : "+v"(lane_e));
+    lane_e &= 63;
+  }
+  const int m_lane = t.m0 + wm * WM + (lane_e & 15);
+  const int n_lane = t.n0 + wn * WN + 4 * (lane_e >> 4);
+  const int r_lane = wm * WM + (lane_e & 15), c_lane = wn * WN + 4 * (lane_e >> 4);   // the same within the tile
   if constexpr (!QOUT) {
     // BF16 epilogue (round to nearest even) through LDS: each wave writes its
     // values into a row-major copy of the tile in the operand slots, idle by
@@ -606,6 +614,10 @@ __device__ __forceinline__ void run_tile(const Tile& t, uint8_t* smem) {
     constexpr int kPitch = G::BN * 2 + 16;   // tile row pitch in bytes
     static_assert(G::BM * kPitch <= G::kLdsBytes, "the output tile fits the operand slots");
     wait_and_barrier<0>();                   // every wave is done with the operand slots
+    // With the accumulators in AGPRs (HW), keep their conversion below the
+    // barrier, tile by tile: converted all at once ahead of it, the packed
+    // values do not fit the VGPRs that remain.
+    if constexpr (HW) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < MS; ++i)
 #pragma unroll
