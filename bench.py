@@ -198,6 +198,22 @@ def _rotations(bytes_per_set, target=600e6):
     return max(2, int(-(-target // bytes_per_set)))
 
 
+def _cast_ceilings(torch, dev, inputs):
+    """Streaming ceilings for the quantizers: PyTorch's own elementwise cast of
+    the same BF16 input to float8_e4m3fn (the same bytes read and written, no
+    amax and no scale). The casts cycle through copies of the input whose
+    inputs and outputs together exceed the Infinity Cache, so that, like the
+    quantizers in the timed steps, they read from HBM. Returns, per kernel
+    name, a function that runs the cast of step i."""
+    out = {}
+    for name, x in inputs.items():
+        n = _rotations(x.numel() * 3)
+        xs = [x.clone() for _ in range(n)]
+        dst = [torch.empty(x.shape, dtype=torch.float8_e4m3fn, device=dev) for _ in range(n)]
+        out[name] = (lambda xs_, dst_: lambda i: dst_[i % len(xs_)].copy_(xs_[i % len(xs_)]))(xs, dst)
+    return out
+
+
 def setup_dense_fprop(torch, fb, dev, M=4096, N=7168, K=7168, fused=False, pow2=False):
     """Quantize X 1x128 and W 128x128, then the GEMM. With fused=True the GEMM
     writes the 1x128 quantization of its result (the next layer's FP8 input)
@@ -223,6 +239,7 @@ def setup_dense_fprop(torch, fb, dev, M=4096, N=7168, K=7168, fused=False, pow2=
             sets[-1]["sQT"] = torch.empty((M // 128, N), dtype=torch.float32, device=dev)
         else:
             sets[-1]["C"] = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    ceilings = _cast_ceilings(torch, dev, {"quant_act_1x128": sets[0]["X"], "quant_w_128x128": sets[0]["W"]})
     L = fb.lib()
     qa = L.fp8_quant_act_1x128_pow2 if pow2 else L.fp8_quant_act_1x128
     qw = L.fp8_quant_w_128x128_pow2 if pow2 else L.fp8_quant_w_128x128
@@ -273,6 +290,7 @@ def setup_dense_fprop(torch, fb, dev, M=4096, N=7168, K=7168, fused=False, pow2=
             gemm: ("TFLOP/s", flops),
         },
         "dominant": gemm,
+        "ceilings": ceilings,
         "config": {"workload": f"dense Fprop projection X[{M}x{K}] bf16 1x128, W[{N}x{K}] bf16 128x128, "
                                f"{out}", "M": M, "N": N, "K": K, "input_rotations": R},
     }
@@ -351,6 +369,9 @@ def setup_backward(torch, fb, dev, M=4096, N=7168, K=7168):
             "dW": torch.empty((N, K), dtype=torch.bfloat16, device=dev),
         })
         del qw, sw
+    ceilings = _cast_ceilings(torch, dev, {"quant_act_1x128(dY)": sets[0]["dY"],
+                                           "quant_act_128x1_T(dY)": sets[0]["dY"],
+                                           "quant_act_128x1_T(X)": sets[0]["X"]})
     L = fb.lib()
     stream = torch.cuda.current_stream(dev).cuda_stream
     state = {"i": 0}
@@ -387,6 +408,7 @@ def setup_backward(torch, fb, dev, M=4096, N=7168, K=7168):
             "gemm_wgrad": ("TFLOP/s", flops),
         },
         "dominant": "gemm_wgrad",
+        "ceilings": ceilings,
         "config": {"workload": f"backward pair: Dgrad dX[{M}x{K}] = dY[{M}x{N}] W, Wgrad dW[{N}x{K}] = dY^T X "
                                f"over {M} tokens", "M": M, "N": N, "K": K, "input_rotations": R},
     }
@@ -424,6 +446,7 @@ def setup_moe(torch, fb, dev):
     L = fb.lib()
     stream = torch.cuda.current_stream(dev).cuda_stream
     A_up, A_dn = d["A_up"], d["A_dn"]
+    ceilings = _cast_ceilings(torch, dev, {"quant_act_1x128(up)": A_up, "quant_act_1x128(down)": A_dn})
 
     def step(timer):
         b = bufs
@@ -452,6 +475,7 @@ def setup_moe(torch, fb, dev):
             "grouped_gemm_down": ("TFLOP/s", fd),
         },
         "dominant": "grouped_gemm_up",
+        "ceilings": ceilings,
         "config": {"workload": f"grouped MoE experts: {E} experts, {Mt} routed rows (8192 tokens x top-8, "
                                f"Dirichlet(0.5)), up {Ku}->{Nu}, down {Kd}->{Nd}", "E": E, "rows": Mt},
     }
@@ -776,6 +800,18 @@ def run_workload(torch, fb, dev, name, steps, warmup, ramp_ms, clock_ms=300.0):
             for _ in range(4):
                 step(warm)
             torch.cuda.synchronize()
+    ceiling_us = {}
+    for n, cast in info.get("ceilings", {}).items():
+        for i in range(4):
+            cast(i)
+        ct = Timer(torch, [n], steps, stream, events)
+        for i in range(steps):
+            ct.mark()
+            cast(i)
+            ct.mark()
+        torch.cuda.synchronize()
+        ceiling_us[n] = percentile(ct.samples_us()[n], 0.5)
+        ct.close()
     kernels = {}
     for n in names:
         unit, work = info["work"][n]
@@ -787,6 +823,11 @@ def run_workload(torch, fb, dev, name, steps, warmup, ramp_ms, clock_ms=300.0):
         kernels[n] = {"us": round(mean, 2), "us_median": round(percentile(ts, 0.5), 2),
                       "us_p10": round(percentile(ts, 0.1), 2), "us_p90": round(percentile(ts, 0.9), 2),
                       unit: round(rate, 1), "frac_of_peak": round(rate / peak, 4)}
+        if n in ceiling_us:
+            # the same bytes through PyTorch's elementwise BF16 -> FP8 cast
+            kernels[n]["cast_ceiling_us_median"] = round(ceiling_us[n], 2)
+            kernels[n]["frac_of_cast_ceiling"] = round(ceiling_us[n] / percentile(ts, 0.5), 3)
+    info.pop("ceilings", None)
     del step
     return info, ms_per_step, kernels, clk.summary(), ramp
 
