@@ -41,6 +41,7 @@
 //   * the tile shape is chosen on the host per problem so that the number of
 //     tiles fills whole rounds of the 256 CUs where possible.
 
+#include <atomic>
 #include <type_traits>
 
 #include "device_common.h"
@@ -883,22 +884,27 @@ int64_t round_cost(int64_t tiles, int cus) {
   return ((tiles + cus - 1) / cus) * (int64_t)G::BM * G::BN;
 }
 
-int device_cus() {
-  static int cus = 0;
-  if (cus == 0) {
-    int dev = 0, n = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
-      cus = n;
-    else
-      cus = 256;
+// Compute units of the device the work runs on (the stream's device; the
+// current device for the null stream), looked up once per device. MI355X
+// has 256; that is also the answer when the query fails.
+int device_cus(hipStream_t stream) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cache[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (stream != nullptr && hipStreamGetDevice(stream, &dev) != hipSuccess) return 256;
+  if (dev < 0 || dev >= kMaxDevices) return 256;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev].store(n, std::memory_order_relaxed);
   }
-  return cus;
+  return n;
 }
 
 // 0: 256x256, 1: 256x224, 2: 224x256
-int pick_dense(int64_t M, int64_t N) {
-  const int cus = device_cus();
+int pick_dense(int64_t M, int64_t N, hipStream_t stream) {
+  const int cus = device_cus(stream);
   auto tiles = [&](int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
   const int64_t c0 = round_cost<Cfg256x256>(tiles(256, 256), cus);
   const int64_t c1 = round_cost<Cfg256x224>(tiles(256, 224), cus);
@@ -1162,7 +1168,7 @@ hipError_t launch_gemm_blockscaled(const uint8_t* A, const float* sA, const uint
                                    const float* sB, int row_mode, uint16_t* C, int64_t M,
                                    int64_t N, int64_t K, hipStream_t stream) {
   using namespace gemm;
-  switch (pick_dense(M, N)) {
+  switch (pick_dense(M, N, stream)) {
     case 1: return launch_dense<Cfg256x224, 0>(A, sA, B, sB, row_mode, C, nullptr, nullptr, M, N, K, stream);
     case 2: return launch_dense<Cfg224x256, 0>(A, sA, B, sB, row_mode, C, nullptr, nullptr, M, N, K, stream);
     default: return launch_dense<Cfg256x256, 0>(A, sA, B, sB, row_mode, C, nullptr, nullptr, M, N, K, stream);
@@ -1173,7 +1179,7 @@ void gemm_blockscaled_tile(int64_t M, int64_t N, int64_t K, int row_mode, int* b
   using namespace gemm;
   (void)K;
   (void)row_mode;
-  switch (pick_dense(M, N)) {
+  switch (pick_dense(M, N, nullptr)) {
     case 1: *bm = Cfg256x224::BM; *bn = Cfg256x224::BN; break;
     case 2: *bm = Cfg224x256::BM; *bn = Cfg224x256::BN; break;
     default: *bm = Cfg256x256::BM; *bn = Cfg256x256::BN; break;
@@ -1195,7 +1201,7 @@ hipError_t launch_gemm_blockscaled_q1x128(const uint8_t* A, const float* sA, con
                                           int64_t M, int64_t N, int64_t K, hipStream_t stream) {
   using namespace gemm;
   // tiles whose columns hold whole 128-column groups: 256x256 or 224x256
-  const int cus = device_cus();
+  const int cus = device_cus(stream);
   const int64_t tn = (N + 255) / 256;
   const int64_t c0 = round_cost<Cfg256x256>(((M + 255) / 256) * tn, cus);
   const int64_t c2 = round_cost<Cfg224x256>(((M + 223) / 224) * tn, cus);
