@@ -59,3 +59,25 @@ def test_default_run_covers_every_configuration():
     names = [wl for _, wl in bench.EXTRA_CONFIGS]
     assert names == ["tiny_fprop", "moe", "decode", "backward"]
     assert all(wl in bench.WORKLOADS for wl in names)
+
+
+def test_cast_ceiling_is_the_plain_cast_of_the_same_tensor(monkeypatch):
+    # the quantizers' streaming ceiling: PyTorch's BF16 -> E4M3 cast of copies
+    # of the input, as many as _rotations asks for (here 3, to keep it small)
+    import torch
+    copies = []
+    monkeypatch.setattr(bench, "_rotations", lambda nbytes: copies.append(nbytes) or 3)
+    x = (torch.randn((64, 256)) * 3).to(torch.bfloat16)
+    run = bench._cast_ceilings(torch, torch.device("cpu"), {"quant_act_1x128": x})["quant_act_1x128"]
+    assert copies == [x.numel() * 3]          # BF16 in, one code byte out
+    want = x.to(torch.float8_e4m3fn).view(torch.uint8)
+    outs = [run(i) for i in range(4)]
+    for got in outs:
+        assert got.dtype == torch.float8_e4m3fn and torch.equal(got.view(torch.uint8), want)
+    assert outs[3].data_ptr() == outs[0].data_ptr() != outs[1].data_ptr()   # cycles through 3 outputs
+
+
+def test_rotations_exceed_the_infinity_cache():
+    for nbytes in (1 << 20, 88_000_000, 300_000_000, 2_000_000_000):
+        n = bench._rotations(nbytes)
+        assert n >= 2 and n * nbytes >= 600e6
