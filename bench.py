@@ -143,21 +143,43 @@ class Timer:
 
 
 class ClockSampler:
-    """Samples the GPU's current shader clock (amdsmi, through torch) every
-    few milliseconds on a background thread while the timed steps run."""
+    """Samples the GPU's shader clock from the SMI on a background thread while
+    the workload runs: the mean over the XCDs of amdsmi's current_gfxclks when
+    it is available, else torch.cuda.clock_rate.
 
-    def __init__(self, torch, period_s=0.005):
+    The SMI refreshes its clock readings only about once a second, so the
+    first readings of a window can still show the clock from before the load
+    (an idle ~100-200 MHz). The window therefore lasts longer than one refresh
+    period, and the leading readings that repeat the window's first value are
+    dropped once a different one has arrived."""
+
+    def __init__(self, torch, period_s=0.02):
         import threading
         self.torch = torch
         self.period = period_s
         self.samples = []
+        self.source = None
         self.stop_evt = threading.Event()
         self.thread = threading.Thread(target=self._run, daemon=True)
+
+    def _read(self):
+        try:
+            import amdsmi
+            handle = self.torch.cuda._get_amdsmi_handler(0)   # the handle torch.cuda.clock_rate(0) reads
+            xs = [float(v) for v in (amdsmi.amdsmi_get_gpu_metrics_info(handle).get("current_gfxclks") or [])
+                  if isinstance(v, (int, float)) and 0 < v < 10000]
+            if xs:
+                self.source = "amdsmi current_gfxclks, mean over XCDs"
+                return sum(xs) / len(xs)
+        except Exception:
+            pass
+        self.source = "torch.cuda.clock_rate"
+        return float(self.torch.cuda.clock_rate(0))
 
     def _run(self):
         while not self.stop_evt.is_set():
             try:
-                mhz = float(self.torch.cuda.clock_rate(0))
+                mhz = self._read()
             except Exception:
                 return
             if mhz > 0:
@@ -173,10 +195,22 @@ class ClockSampler:
         self.thread.join()
 
     def summary(self):
-        if not self.samples:
-            return None
-        xs = sorted(self.samples)
-        return {"median_mhz": xs[len(xs) // 2], "min_mhz": xs[0], "max_mhz": xs[-1], "samples": len(xs)}
+        return clock_summary(self.samples, self.source)
+
+
+def clock_summary(samples, source=None):
+    """Median, range and count of the clock readings after dropping the stale
+    leading run (readings equal to the first one, when a later reading
+    differs); None without readings."""
+    if not samples:
+        return None
+    k = 0
+    while k < len(samples) and samples[k] == samples[0]:
+        k += 1
+    used = samples[k:] if k < len(samples) else samples
+    xs = sorted(used)
+    return {"median_mhz": round(xs[len(xs) // 2], 1), "min_mhz": round(xs[0], 1), "max_mhz": round(xs[-1], 1),
+            "samples": len(xs), "stale_dropped": len(samples) - len(used), "source": source}
 
 
 def percentile(xs, q):
@@ -752,7 +786,7 @@ def cpu_baseline(workload):
             "sample": f"one Fprop step at {M}x{N}x{K}: quantize X 1x128 and W 128x128, {what}; {dt:.1f} s"}
 
 
-def run_workload(torch, fb, dev, name, steps, warmup, ramp_ms, clock_ms=300.0):
+def run_workload(torch, fb, dev, name, steps, warmup, ramp_ms, clock_ms=1500.0):
     """Set up one workload, ramp the clocks, warm up, time `steps` steps.
 
     Returns the step function's info, the wall-clock ms per step, per-kernel
@@ -788,8 +822,8 @@ def run_workload(torch, fb, dev, name, steps, warmup, ramp_ms, clock_ms=300.0):
     samples = timer.samples_us()
     timer.close()
     # The shader clock under this workload's load: the same steps, untimed, for
-    # clock_ms more while the clock is sampled (the sampled value is an average
-    # over the sensor's own period, so the window is longer than that period).
+    # clock_ms more while the clock is sampled (the SMI refreshes its reading
+    # about once a second, so the window is longer than that).
     try:
         torch.cuda.clock_rate(0)        # initializes the query before the window
     except Exception:
@@ -904,7 +938,7 @@ def main():
     if args.workload == "dense_fprop" and not args.no_configs:
         configs = {}
         for key, wl in EXTRA_CONFIGS:
-            cinfo, cms, ck, cclk, _ = run_workload(torch, fb, dev, wl, args.config_steps, 3, 100.0)
+            cinfo, cms, ck, cclk, _ = run_workload(torch, fb, dev, wl, args.config_steps, 3, 100.0, 1200.0)
             configs[key] = {"workload": cinfo["config"]["workload"], "ms_per_step": round(cms, 4),
                             "kernels": ck, "sclk_median_mhz": cclk["median_mhz"] if cclk else None}
             torch.cuda.empty_cache()

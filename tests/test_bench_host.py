@@ -81,3 +81,13 @@ def test_rotations_exceed_the_infinity_cache():
     for nbytes in (1 << 20, 88_000_000, 300_000_000, 2_000_000_000):
         n = bench._rotations(nbytes)
         assert n >= 2 and n * nbytes >= 600e6
+
+
+def test_clock_summary_drops_the_stale_leading_readings():
+    # the SMI refreshes about once a second: readings from before the load
+    # repeat until the first refresh and are dropped once a new one arrives
+    s = bench.clock_summary([95.0, 95.0, 95.0, 1969.0, 1969.0, 1950.0], "test")
+    assert s["median_mhz"] == 1969.0 and s["min_mhz"] == 1950.0 and s["samples"] == 3 and s["stale_dropped"] == 3
+    s = bench.clock_summary([2079.0] * 5)          # no refresh seen: every reading kept
+    assert s["median_mhz"] == 2079.0 and s["samples"] == 5 and s["stale_dropped"] == 0
+    assert bench.clock_summary([]) is None
