@@ -10,6 +10,10 @@ against the oracle, beyond the hand-picked cases of the other files.
 * Quantizers: 1x128 (any M, F32 or BF16), 128x128 (with and without the
   transposed copy) and 128x1 transposed (any C) on values whose magnitude
   varies per column and per row, with outliers, bit for bit.
+* The fused quantizing epilogues (1x128, and both layouts), the power-of-two
+  quantizers and the MFMA-scaled GEMM on their outputs, the grouped 128x1
+  quantizers and the per-expert Wgrad on their outputs, and the MoE dispatch
+  payload (routing, codes, scales) and the combine.
 
 Acceptance bound for the GEMMs: |C - ref| <= 4e-3 * sum_k |a_k b_k| + ulp_bf16(ref).
 """
@@ -101,8 +105,9 @@ def _values(rng, shape, dtype):
     a few outliers x1000 and some exact zeros."""
     x = rng.standard_normal(shape) * np.exp2(rng.uniform(-20, 20, (1, shape[1])))
     x *= np.exp2(rng.uniform(-6, 6, (shape[0], 1)))
-    x.flat[rng.integers(0, x.size, max(1, x.size // 500))] *= 1000.0
-    x.flat[rng.integers(0, x.size, max(1, x.size // 300))] = 0.0
+    if x.size:
+        x.flat[rng.integers(0, x.size, max(1, x.size // 500))] *= 1000.0
+        x.flat[rng.integers(0, x.size, max(1, x.size // 300))] = 0.0
     t = torch.from_numpy(x.astype(np.float32))
     return t.to(torch.bfloat16) if dtype == "bf16" else t
 
@@ -145,3 +150,123 @@ def test_random_quant_act_128x1_T(dev, seed):
     qo, so = oracle.quant_act_128x1_T(to_oracle(X))
     assert_codes_equal(u8(qT), qo, f"seed {seed}: 128x1T {M}x{C} {dtype} codes")
     assert_scales_equal(sT.cpu().numpy(), so, f"seed {seed}: 128x1T {M}x{C} {dtype} scales")
+
+
+# ---------------------------------------------------------------------------
+# the other entry points: fused quantizing epilogues, power-of-two path,
+# grouped backward, dispatch and combine
+# ---------------------------------------------------------------------------
+
+def _to(dev, *arrays):
+    return [torch.from_numpy(np.ascontiguousarray(a)).to(dev) for a in arrays]
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_fused_epilogues(dev, seed):
+    # 1x128 epilogue for any M; both layouts when M is a multiple of 128. The
+    # fused codes and scales are the oracle's quantization of the GEMM's BF16 result.
+    rng = np.random.default_rng(9300 + seed)
+    both = seed % 2 == 1
+    M = 128 * int(rng.integers(1, 7)) if both else int(rng.integers(1, 800))
+    N, K = 128 * int(rng.integers(1, 9)), 128 * int(rng.integers(1, 9))
+    mode = int(rng.integers(0, 2))
+    A, B = _codes(rng, (M, K)), _codes(rng, (N, K))
+    sA = _scales(rng, (K // 128, M))
+    sB = _scales(rng, (N // 128, K // 128) if mode == MODE_BLOCK else (K // 128, N))
+    args = (*_to(dev, A, sA, B, sB), mode)
+    C = fb.fp8_gemm_blockscaled(*args)
+    out = fb.fp8_gemm_blockscaled_q1x128_q128x1T(*args) if both else fb.fp8_gemm_blockscaled_q1x128(*args)
+    torch.cuda.synchronize()
+    what = f"seed {seed}: fused {'both' if both else '1x128'} {M}x{N}x{K} mode {mode}"
+    ref, absref = oracle.gemm_ref(A, sA, B, sB, mode)
+    _check(C, ref, absref, what + " BF16 result")
+    qo, so = oracle.quant_act_1x128(bf16_bits(C))
+    assert_codes_equal(u8(out[0]), qo, what + " 1x128 codes")
+    assert_scales_equal(out[1].cpu().numpy(), so, what + " 1x128 scales")
+    if both:
+        qto, sto = oracle.quant_act_128x1_T(bf16_bits(C))
+        assert_codes_equal(u8(out[2]), qto, what + " 128x1 codes")
+        assert_scales_equal(out[3].cpu().numpy(), sto, what + " 128x1 scales")
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_pow2_path(dev, seed):
+    # power-of-two quantizers bit for bit, then the MFMA-scaled GEMM on their outputs
+    rng = np.random.default_rng(9400 + seed)
+    M, N, K = int(rng.integers(1, 700)), 128 * int(rng.integers(1, 9)), 128 * int(rng.integers(1, 9))
+    dtype = ("bf16", "f32")[seed % 2]
+    X, W = _values(rng, (M, K), dtype), _values(rng, (N, K), dtype)
+    qx, sx = fb.fp8_quant_act_1x128(X.to(dev), pow2=True)
+    qw, sw = fb.fp8_quant_w_128x128(W.to(dev), pow2=True)
+    C = fb.fp8_gemm_blockscaled(qx, sx, qw, sw, MODE_BLOCK, pow2=True)
+    torch.cuda.synchronize()
+    what = f"seed {seed}: pow2 {M}x{N}x{K} {dtype}"
+    qxo, sxo = oracle.quant_act_1x128(to_oracle(X), pow2=True)
+    qwo, swo = oracle.quant_w_128x128(to_oracle(W), pow2=True)
+    assert_codes_equal(u8(qx), qxo, what + " activation codes")
+    assert_scales_equal(sx.cpu().numpy(), sxo, what + " activation scales")
+    assert_codes_equal(u8(qw), qwo, what + " weight codes")
+    assert_scales_equal(sw.cpu().numpy(), swo, what + " weight scales")
+    ref, absref = oracle.gemm_ref(qxo, sxo, qwo, swo, MODE_BLOCK)
+    _check(C, ref, absref, what + " GEMM")
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_grouped_backward(dev, seed):
+    # BF16/F32 dY and X over ragged experts -> grouped 128x1 quantizers
+    # (bit for bit) -> per-expert Wgrad on their outputs (within the bound)
+    rng = np.random.default_rng(9500 + seed)
+    counts = _expert_counts(rng)
+    E = len(counts)
+    off = np.zeros(E + 1, np.int32)
+    off[1:] = np.cumsum(counts)
+    M = int(off[-1])
+    N, K = 128 * int(rng.integers(1, 5)), 128 * int(rng.integers(1, 5))
+    dtype = ("bf16", "f32")[seed % 2]
+    dY, X = _values(rng, (M, N), dtype), _values(rng, (M, K), dtype)
+    offd = torch.from_numpy(off).to(dev)
+    qa, sa = fb.fp8_quant_act_128x1_T_grouped(dY.to(dev), offd)
+    qb, sb = fb.fp8_quant_act_128x1_T_grouped(X.to(dev), offd)
+    dW = fb.fp8_grouped_gemm_wgrad(qa, sa, qb, sb, offd, M)
+    torch.cuda.synchronize()
+    what = f"seed {seed}: grouped backward counts {counts.tolist()} N={N} K={K} {dtype}"
+    qao, sao = oracle.quant_act_128x1_T_grouped(to_oracle(dY), off)
+    qbo, sbo = oracle.quant_act_128x1_T_grouped(to_oracle(X), off)
+    G = sao.shape[0]
+    assert_codes_equal(u8(qa[:, :128 * G]), qao, what + " dY codes")
+    assert_scales_equal(sa[:G].cpu().numpy(), sao, what + " dY scales")
+    assert_codes_equal(u8(qb[:, :128 * G]), qbo, what + " X codes")
+    assert_scales_equal(sb[:G].cpu().numpy(), sbo, what + " X scales")
+    ref, absref = oracle.grouped_wgrad_ref(u8(qa), sa.cpu().numpy(), u8(qb), sb.cpu().numpy(), off)
+    _check(dW, ref, absref, what + " Wgrad")
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_dispatch_and_combine(dev, seed):
+    rng = np.random.default_rng(9600 + seed)
+    T, K = int(rng.integers(1, 1500)), 128 * int(rng.integers(1, 9))
+    E = int(rng.integers(1, 300))
+    topk = int(rng.integers(1, min(E, 8) + 1))
+    p = rng.dirichlet(np.full(E, 0.3)) + 1e-3
+    p /= p.sum()
+    ids = np.stack([rng.choice(E, topk, replace=False, p=p) for _ in range(T)]).astype(np.int32)
+    dtype = ("bf16", "f32")[seed % 2]
+    x = _values(rng, (T, K), dtype)
+    q, s, off, pos, src = fb.fp8_moe_dispatch(x.to(dev), torch.from_numpy(ids).to(dev), E)
+    torch.cuda.synchronize()
+    what = f"seed {seed}: dispatch T={T} K={K} E={E} topk={topk} {dtype}"
+    qo, so, offo, poso, srco = oracle.dispatch_quant(to_oracle(x), ids, E)
+    assert np.array_equal(off.cpu().numpy(), offo), what + " offsets"
+    assert np.array_equal(pos.cpu().numpy(), poso), what + " pos"
+    assert np.array_equal(src.cpu().numpy(), srco), what + " src_row"
+    assert_codes_equal(u8(q), qo, what + " codes")
+    assert_scales_equal(s.cpu().numpy(), so, what + " scales")
+    # combine expert outputs Y (BF16, in the dispatched row order) with random weights
+    N = 128 * int(rng.integers(1, 9))
+    Y = torch.from_numpy(rng.standard_normal((T * topk, N)).astype(np.float32) * 3).to(torch.bfloat16)
+    w = torch.from_numpy(rng.random((T, topk)).astype(np.float32))
+    out = fb.fp8_moe_combine(Y.to(dev), pos, w.to(dev))
+    torch.cuda.synchronize()
+    ref, absref = oracle.combine_ref(oracle.bf16_bits_to_f64(bf16_bits(Y)), poso, w.numpy().astype(np.float64))
+    ok, worst = oracle.check_combine(bf16_bits(out), ref, absref, topk)
+    assert ok.all(), f"{what} combine: {int((~ok).sum())} outside the bound (worst {worst:.3g})"
