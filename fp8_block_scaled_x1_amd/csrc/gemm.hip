@@ -803,16 +803,14 @@ __global__ __launch_bounds__(G::kThreads, 1) void gemm_kernel(const uint8_t* __r
 // ceil(rows/BM) x ceil(N/BN), numbered expert-major; experts with min_rows
 // rows or fewer have none (the decode kernel takes them). The grid is an
 // upper bound on the total; workgroups past the last tile exit at once.
-// Workgroup bid of nblocks (bid % 8 is its XCD) of the grouped tile path:
-// experts with more than min_rows rows, tiles numbered expert-major.
 template <class G>
-__device__ __forceinline__ void grouped_tile_block(int bid, int nblocks, const uint8_t* __restrict__ A,
-                                                   const float* __restrict__ sA, const uint8_t* __restrict__ B,
-                                                   const float* __restrict__ sB, uint16_t* __restrict__ C,
-                                                   const int32_t* __restrict__ offsets, int E, int M_total, int N,
-                                                   int K, int min_rows, uint8_t* smem) {
+__global__ __launch_bounds__(G::kThreads, 1) void grouped_gemm_kernel(
+    const uint8_t* __restrict__ A, const float* __restrict__ sA, const uint8_t* __restrict__ B,
+    const float* __restrict__ sB, uint16_t* __restrict__ C, const int32_t* __restrict__ offsets,
+    int E, int M_total, int N, int K, int min_rows) {
+  __shared__ __align__(16) uint8_t smem[G::kLdsBytes];
   const int tiles_n = (N + G::BN - 1) / G::BN;
-  const int pid = xcd_remap(bid, nblocks);
+  const int pid = xcd_remap(blockIdx.x, gridDim.x);
   // the expert of tile pid (tiles numbered expert-major)
   const ExpertSlot es = locate_expert(offsets, E, M_total, pid, G::BM, tiles_n, min_rows);
   if (es.e < 0) return;
@@ -828,15 +826,6 @@ __device__ __forceinline__ void grouped_tile_block(int bid, int nblocks, const u
   t.m0 = r0 + tm * G::BM; t.row_end = r1;
   t.n0 = tn * G::BN; t.N = N; t.K = K; t.ld = K;
   run_tile<G, 0>(t, smem);
-}
-
-template <class G>
-__global__ __launch_bounds__(G::kThreads, 1) void grouped_gemm_kernel(
-    const uint8_t* __restrict__ A, const float* __restrict__ sA, const uint8_t* __restrict__ B,
-    const float* __restrict__ sB, uint16_t* __restrict__ C, const int32_t* __restrict__ offsets,
-    int E, int M_total, int N, int K, int min_rows) {
-  __shared__ __align__(16) uint8_t smem[G::kLdsBytes];
-  grouped_tile_block<G>(blockIdx.x, gridDim.x, A, sA, B, sB, C, offsets, E, M_total, N, K, min_rows, smem);
 }
 
 // Per-expert Wgrad: C[e] = A_e B_e^T over expert e's tokens, row-mode scales.
@@ -942,8 +931,7 @@ hipError_t launch_dense(const uint8_t* A, const float* sA, const uint8_t* B, con
 // Decode-shaped grouped GEMM (few activation rows per expert, so the weights
 // are the stream). One workgroup per (expert, 128 weight rows) covers all of
 // the expert's rows, up to 256 per pass, so every weight byte is read once
-// (the launcher leaves experts with more rows to the tile path, in the same
-// launch: grouped_mixed_kernel). Each of the 8 waves streams
+// (experts with more rows take further passes). Each of the 8 waves streams
 // its own 16 weight rows from HBM straight into MFMA operand registers, kDB
 // chunks ahead of use. The activation chunk (the pass's rows x 128 bytes and
 // their sA) goes through registers into a double-buffered, swizzled LDS tile
@@ -1106,22 +1094,19 @@ __device__ __forceinline__ void run_pass(const Pass a, uint8_t* smem) {
 }
 }  // namespace dec
 
-// Workgroup bid of nblocks (bid % 8 is its XCD) of the weight-streaming path;
-// ids past E * ceil(N / 128) have no work. Experts with more than max_rows
-// rows are left to the tile path.
-__device__ __forceinline__ void grouped_decode_block(int bid, int nblocks, const uint8_t* __restrict__ A,
-                                                     const float* __restrict__ sA, const uint8_t* __restrict__ B,
-                                                     const float* __restrict__ sB, uint16_t* __restrict__ C,
-                                                     const int32_t* __restrict__ offsets, int E, int M_total, int N,
-                                                     int K, int max_rows, uint8_t* smem) {
+// Experts with more than max_rows rows are left to the tile kernel.
+__global__ __launch_bounds__(dec::kThreads, 1) void grouped_decode_kernel(
+    const uint8_t* __restrict__ A, const float* __restrict__ sA, const uint8_t* __restrict__ B,
+    const float* __restrict__ sB, uint16_t* __restrict__ C, const int32_t* __restrict__ offsets, int E,
+    int M_total, int N, int K, int max_rows) {
+  __shared__ __align__(16) uint8_t smem[dec::kLds];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nblk = (N + dec::kBN - 1) / dec::kBN;
   // consecutive ids on one XCD: an expert's weight blocks share that XCD's L2
   // copy of its activations instead of every XCD fetching them
-  const int pid = xcd_remap(bid, nblocks);
+  const int pid = xcd_remap(blockIdx.x, gridDim.x);
   const int slot = pid / nblk, nb = pid % nblk;
-  if (slot >= E) return;
   auto rows_of = [&](int x, int& lo, int& hi) {
     lo = min(max(offsets[x], 0), M_total);
     hi = min(max(offsets[x + 1], lo), M_total);
@@ -1175,27 +1160,6 @@ __device__ __forceinline__ void grouped_decode_block(int bid, int nblocks, const
       default: dec::run_pass<16>(a, smem); break;
     }
   }
-}
-
-// Decode-shaped batches in one launch: workgroups below n_dec take the
-// weight-streaming path for the experts of at most dec::kBM rows, the rest
-// the tile path for the experts with more (a skewed batch); when there are
-// none those workgroups find no tile and exit. n_dec is a multiple of 8, so
-// both paths keep their XCD-aware numbering.
-template <class G>
-__global__ __launch_bounds__(dec::kThreads, 1) void grouped_mixed_kernel(
-    const uint8_t* __restrict__ A, const float* __restrict__ sA, const uint8_t* __restrict__ B,
-    const float* __restrict__ sB, uint16_t* __restrict__ C, const int32_t* __restrict__ offsets, int E,
-    int M_total, int N, int K, int n_dec) {
-  static_assert(G::kThreads == dec::kThreads, "both paths run 8 waves");
-  constexpr int kLds = G::kLdsBytes > dec::kLds ? G::kLdsBytes : dec::kLds;
-  __shared__ __align__(16) uint8_t smem[kLds];
-  const int bid = blockIdx.x;
-  if (bid < n_dec)
-    grouped_decode_block(bid, n_dec, A, sA, B, sB, C, offsets, E, M_total, N, K, dec::kBM, smem);
-  else
-    grouped_tile_block<G>(bid - n_dec, (int)gridDim.x - n_dec, A, sA, B, sB, C, offsets, E, M_total, N, K,
-                          dec::kBM, smem);
 }
 
 }  // namespace gemm
@@ -1261,24 +1225,35 @@ hipError_t launch_grouped_gemm_blockscaled(const uint8_t* A, const float* sA, co
   using namespace gemm;
   using G = Cfg256x256;
   const int64_t tiles_n = (N + G::BN - 1) / G::BN;
-  // Many rows per expert on average: the tile kernel for every expert; every
-  // expert adds at most one partial m-tile beyond M_total / BM.
-  if (M_total >= (int64_t)E * dec::kBM) {
+  // More than 256 rows per expert on average: the tile kernel for every
+  // expert; every expert adds at most one partial m-tile beyond M_total / BM.
+  // (At 256 rows per expert the weight-streaming kernel below is the faster:
+  // 384 against 450 us for 32 experts of 256 rows, N 4096, K 7168; routing a
+  // MoE batch's few small experts to it, in a launch of its own ahead of the
+  // tile kernel, costs more than the tile rounds it saves: 2,041 against
+  // 1,966 us for the MoE up projection.)
+  if (M_total > (int64_t)E * dec::kBM) {
     const int64_t tiles = ((M_total + G::BM - 1) / G::BM + E) * tiles_n;
     hipLaunchKernelGGL((grouped_gemm_kernel<G>), dim3((unsigned)tiles), dim3(G::kThreads), 0, stream, A, sA, B,
                        sB, C, offsets, E, (int)M_total, (int)N, (int)K, 0);
     return hipGetLastError();
   }
-  // Few rows per expert on average (decode): the weight-streaming path for
+  // Few rows per expert on average (decode): the weight-streaming kernel for
   // experts of at most one 256-row pass, which reads their weights once
   // whatever their rows; the offsets live on the device, so any expert with
-  // more rows (a skewed batch) is left to the tile path, in the same launch:
-  // at most M_total / 257 such experts, adding at most one partial m-tile each.
-  const int64_t n_dec = ((int64_t)E * ((N + dec::kBN - 1) / dec::kBN) + kXcds - 1) / kXcds * kXcds;
+  // more rows (a skewed batch) is left to the tile kernel, launched behind it
+  // for those experts only: at most M_total / 257 of them, adding at most
+  // one partial m-tile each.
+  const int64_t blocks = (int64_t)E * ((N + dec::kBN - 1) / dec::kBN);
+  hipLaunchKernelGGL(grouped_decode_kernel, dim3((unsigned)blocks), dim3(dec::kThreads), 0, stream, A, sA, B, sB,
+                     C, offsets, E, (int)M_total, (int)N, (int)K, dec::kBM);
   const int64_t big = M_total / (dec::kBM + 1);
-  const int64_t tiles = big > 0 ? ((M_total + G::BM - 1) / G::BM + big) * tiles_n : 0;
-  hipLaunchKernelGGL((grouped_mixed_kernel<G>), dim3((unsigned)(n_dec + tiles)), dim3(dec::kThreads), 0, stream, A,
-                     sA, B, sB, C, offsets, E, (int)M_total, (int)N, (int)K, (int)n_dec);
+  if (big == 0) return hipGetLastError();
+  const hipError_t e1 = hipGetLastError();
+  if (e1 != hipSuccess) return e1;
+  const int64_t tiles = ((M_total + G::BM - 1) / G::BM + big) * tiles_n;
+  hipLaunchKernelGGL((grouped_gemm_kernel<G>), dim3((unsigned)tiles), dim3(G::kThreads), 0, stream, A, sA, B, sB,
+                     C, offsets, E, (int)M_total, (int)N, (int)K, dec::kBM);
   return hipGetLastError();
 }
 

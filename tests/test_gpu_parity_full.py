@@ -6,8 +6,8 @@
 * The dense Fprop, Dgrad and Wgrad layers at their real sizes are compared on
   one full output row per m-tile, the row's offset inside its tile moving
   from tile to tile, so every wave row and both halves of every tile are seen.
-* The grouped GEMM's tile kernel (chosen when the experts average 256 rows or
-  more) on ragged experts that include empty ones, and skewed batches whose
+* The grouped GEMM's tile kernel (chosen when the experts average more than
+  256 rows) on ragged experts that include empty ones, and skewed batches whose
   few large experts go to the tile kernel while the rest take the
   weight-streaming kernel.
 * The MoE activation and expert-weight quantizers at their full sizes
@@ -129,14 +129,14 @@ def test_backward_pair_full_size_rows_per_tile(dev):
 
 @pytest.mark.parametrize("counts,N,K", [
     ([0, 900, 0, 250], 512, 512),                               # empty first and inner experts
-    ([300, 0, 0, 0, 1200, 17, 0, 540], 384, 256),               # M_total = 2057 >= 256 * 8
+    ([300, 0, 0, 0, 1200, 17, 0, 540], 384, 256),               # M_total = 2057 > 256 * 8
     ([0, 0, 2100, 0], 256, 384),                                 # one expert holds every row
 ])
 def test_grouped_tile_kernel_with_empty_experts(dev, counts, N, K):
     off = np.zeros(len(counts) + 1, np.int32)
     off[1:] = np.cumsum(counts)
     M, E = int(off[-1]), len(counts)
-    assert M >= 256 * E, "the case must take the grouped tile kernel"
+    assert M > 256 * E, "the case must take the grouped tile kernel"
     seed = M + N + K
     A, sA = _codes((M, K), seed), _scales((K // 128, M), seed + 1)
     B, sB = _codes((E, N, K), seed + 2), _scales((E, N // 128, K // 128), seed + 3)
