@@ -90,6 +90,13 @@ struct Cfg {
 using Cfg256x256 = Cfg<256, 256, 2, 4, 2, 2>;
 using Cfg256x224 = Cfg<256, 224, 4, 2, 3, 2>;
 using Cfg224x256 = Cfg<224, 256, 2, 4, 2, 3>;
+// Smaller tiles for problems with few output tiles (skinny M, few tokens),
+// which the large tiles would leave on a fraction of the CUs: 128x256, waves
+// 2x4 of 64x64; 128x128, waves 4x2 of 32x64; 64x64, 4 waves 2x2 of 32x32.
+// The two smallest leave registers and LDS for two or more workgroups per CU.
+using Cfg128x256 = Cfg<128, 256, 2, 4, 2, 2>;
+using Cfg128x128 = Cfg<128, 128, 4, 2, 2, 2>;
+using Cfg64x64 = Cfg<64, 64, 2, 2, 2, 2>;
 // 256x256 with 4 waves of 128x128 (one per SIMD, up to 512 registers each):
 // only for the hardware-scaled variant, whose accumulators the MFMA updates
 // in place (they can live in AGPRs), so no promotion needs them in VGPRs
@@ -902,15 +909,39 @@ int device_cus(hipStream_t stream) {
   return n;
 }
 
-// 0: 256x256, 1: 256x224, 2: 224x256
-int pick_dense(int64_t M, int64_t N, hipStream_t stream) {
+// Dense tile shapes, in the order pick_dense numbers them, with the estimate
+// it compares (MI355X, K = 7168; measured): a tile takes at least `lat` us
+// even alone on its CU, a CU kept busy with such tiles produces at most
+// `thr` output elements per us (smaller tiles share a CU between workgroups
+// but re-read their operands more often), and each round of tiles adds about
+// 4 us (its first loads and its epilogue), where a round is `per_cu` tiles:
+// as many workgroups as fit on a CU together (LDS and registers).
+struct TileEst {
+  int bm, bn, per_cu;
+  double lat, thr;
+};
+enum DenseTile { kT256x256, kT256x224, kT224x256, kT128x256, kT128x128, kT64x64, kDenseTiles };
+constexpr TileEst kTileEst[kDenseTiles] = {{256, 256, 1, 80.0, 650.0}, {256, 224, 1, 70.0, 637.0},
+                                           {224, 256, 1, 70.0, 637.0}, {128, 256, 1, 54.0, 536.0},
+                                           {128, 128, 2, 43.0, 531.0}, {64, 64, 4, 33.0, 333.0}};
+
+int pick_dense(int64_t M, int64_t N, int64_t K, hipStream_t stream) {
   const int cus = device_cus(stream);
-  auto tiles = [&](int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
-  const int64_t c0 = round_cost<Cfg256x256>(tiles(256, 256), cus);
-  const int64_t c1 = round_cost<Cfg256x224>(tiles(256, 224), cus);
-  const int64_t c2 = round_cost<Cfg224x256>(tiles(224, 256), cus);
-  if (c0 <= c1 && c0 <= c2) return 0;
-  return c1 <= c2 ? 1 : 2;
+  const double k = (double)K / 7168.0;
+  int best = 0;
+  double best_t = 0.0;
+  for (int i = 0; i < kDenseTiles; ++i) {
+    const TileEst& c = kTileEst[i];
+    const int64_t tiles = ((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
+    const int64_t per_cu = (tiles + cus - 1) / cus;
+    const int64_t rounds = (per_cu + c.per_cu - 1) / c.per_cu;
+    const double t = std::max(c.lat * k, (double)per_cu * c.bm * c.bn / c.thr * k) + 4.0 * (double)rounds;
+    if (i == 0 || t < best_t) {
+      best = i;
+      best_t = t;
+    }
+  }
+  return best;
 }
 
 template <class G, int QOUT, int HW = 0>
@@ -1168,22 +1199,22 @@ hipError_t launch_gemm_blockscaled(const uint8_t* A, const float* sA, const uint
                                    const float* sB, int row_mode, uint16_t* C, int64_t M,
                                    int64_t N, int64_t K, hipStream_t stream) {
   using namespace gemm;
-  switch (pick_dense(M, N, stream)) {
-    case 1: return launch_dense<Cfg256x224, 0>(A, sA, B, sB, row_mode, C, nullptr, nullptr, M, N, K, stream);
-    case 2: return launch_dense<Cfg224x256, 0>(A, sA, B, sB, row_mode, C, nullptr, nullptr, M, N, K, stream);
+  switch (pick_dense(M, N, K, stream)) {
+    case kT256x224: return launch_dense<Cfg256x224, 0>(A, sA, B, sB, row_mode, C, nullptr, nullptr, M, N, K, stream);
+    case kT224x256: return launch_dense<Cfg224x256, 0>(A, sA, B, sB, row_mode, C, nullptr, nullptr, M, N, K, stream);
+    case kT128x256: return launch_dense<Cfg128x256, 0>(A, sA, B, sB, row_mode, C, nullptr, nullptr, M, N, K, stream);
+    case kT128x128: return launch_dense<Cfg128x128, 0>(A, sA, B, sB, row_mode, C, nullptr, nullptr, M, N, K, stream);
+    case kT64x64: return launch_dense<Cfg64x64, 0>(A, sA, B, sB, row_mode, C, nullptr, nullptr, M, N, K, stream);
     default: return launch_dense<Cfg256x256, 0>(A, sA, B, sB, row_mode, C, nullptr, nullptr, M, N, K, stream);
   }
 }
 
 void gemm_blockscaled_tile(int64_t M, int64_t N, int64_t K, int row_mode, int* bm, int* bn) {
   using namespace gemm;
-  (void)K;
   (void)row_mode;
-  switch (pick_dense(M, N, nullptr)) {
-    case 1: *bm = Cfg256x224::BM; *bn = Cfg256x224::BN; break;
-    case 2: *bm = Cfg224x256::BM; *bn = Cfg224x256::BN; break;
-    default: *bm = Cfg256x256::BM; *bn = Cfg256x256::BN; break;
-  }
+  const int t = pick_dense(M, N, K, nullptr);
+  *bm = kTileEst[t].bm;
+  *bn = kTileEst[t].bn;
 }
 
 hipError_t launch_gemm_blockscaled_pow2(const uint8_t* A, const float* sA, const uint8_t* B,

@@ -225,3 +225,23 @@ def test_noalloc_dispatch_validation(L):
     # E * ceil(T*topk/1024) * 4 bytes: 1024 experts x 257 blocks > 2^20
     assert d(P, 1, 257 * 128, 128, P, 8, 1024, P, P, P, P, P, NULL) == -8
     assert fb.status_string(-8).startswith("the problem needs more scratch memory")
+
+
+def test_tile_query_follows_the_shape(L):
+    # host-side choice, no device needed (a 256-CU MI355X is assumed when no
+    # device answers): skinny problems take the small tiles that spread them
+    # over every CU, full-size layers the large ones
+    import ctypes
+    bm, bn = ctypes.c_int(), ctypes.c_int()
+
+    def tile(M, N, K):
+        assert L.fp8_gemm_blockscaled_tile(M, N, K, 0, ctypes.byref(bm), ctypes.byref(bn)) == 0
+        return bm.value, bn.value
+
+    assert tile(64, 7168, 7168) == (64, 64)            # a few tokens: 112 tiles of 256 would idle 144 CUs
+    assert tile(512, 7168, 7168) == (128, 128)
+    assert tile(4096, 2048, 7168) == (128, 256)
+    assert tile(4096, 7168, 7168) == (256, 224)        # 512 tiles: two full rounds
+    assert tile(4096, 4096, 4096) == (256, 256)
+    assert tile(7168, 4096, 4096) == (224, 256)
+    assert tile(1, 128, 128) == (64, 64)

@@ -58,7 +58,10 @@ def _check(C, ref, absref, what):
 TILE_CASES = [((4096, 4096, 256), (256, 256)),
               ((4096, 7168, 256), (256, 224)),
               ((7168, 2048, 256), (224, 256)),
-              ((7168, 4096, 128), (224, 256))]
+              ((7168, 4096, 128), (224, 256)),
+              ((777, 5120, 128), (128, 256)),      # ragged last m-tile (9 rows)
+              ((1700, 2048, 128), (128, 128)),     # ragged last m-tile (36 rows)
+              ((300, 640, 256), (64, 64))]         # ragged last m-tile (44 rows)
 
 
 def test_tile_cases_cover_every_tile(dev):
