@@ -326,6 +326,24 @@ __device__ __forceinline__ ExpertSlot locate_expert(const int32_t* __restrict__ 
   return r;
 }
 
+// Units (as above) of all experts together; wave-uniform.
+__device__ __forceinline__ int total_units(const int32_t* __restrict__ off, int E, int M_total, int unit_rows,
+                                           int mult, int min_rows = 0) {
+  const int lane = threadIdx.x & 63;
+  int sum = 0;
+  for (int e0 = 0; e0 < E; e0 += 64) {
+    const int e = e0 + lane;
+    if (e < E) {
+      const int a = min(max(off[e], 0), M_total);
+      const int b = min(max(off[e + 1], a), M_total);
+      sum += b - a > min_rows ? ((b - a + unit_rows - 1) / unit_rows) * mult : 0;
+    }
+  }
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) sum += __shfl_xor(sum, d, 64);
+  return __builtin_amdgcn_readfirstlane(sum);
+}
+
 // Units (as above, mult = 1) of the experts before expert e, with e's own
 // row range; wave-uniform.
 __device__ __forceinline__ ExpertSlot units_before(const int32_t* __restrict__ off, int M_total, int e,

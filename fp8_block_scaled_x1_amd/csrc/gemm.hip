@@ -97,6 +97,15 @@ using Cfg224x256 = Cfg<224, 256, 2, 4, 2, 3>;
 using Cfg128x256 = Cfg<128, 256, 2, 4, 2, 2>;
 using Cfg128x128 = Cfg<128, 128, 4, 2, 2, 2>;
 using Cfg64x64 = Cfg<64, 64, 2, 2, 2, 2>;
+// The same two with both rings three deep: loads run two chunks ahead, which
+// a lone workgroup on its CU needs to cover the load latency, at the price of
+// co-residency (128x128: one workgroup per CU; 64x64: three)
+using Cfg128x128d3 = Cfg<128, 128, 4, 2, 3, 3>;
+using Cfg64x64d3 = Cfg<64, 64, 2, 2, 3, 3>;
+// Subtiles of the grouped GEMM's tail kernel, and how many of its workgroups
+// share a CU (LDS and registers)
+using TailCfg = Cfg64x64d3;
+constexpr int kTailPerCu = 3;
 // 256x256 with 4 waves of 128x128 (one per SIMD, up to 512 registers each):
 // only for the hardware-scaled variant, whose accumulators the MFMA updates
 // in place (they can live in AGPRs), so no promotion needs them in VGPRs
@@ -809,15 +818,32 @@ __global__ __launch_bounds__(G::kThreads, 1) void gemm_kernel(const uint8_t* __r
 // Per-expert tiles: expert e owns rows [off[e], off[e+1]); its tiles are
 // ceil(rows/BM) x ceil(N/BN), numbered expert-major; experts with min_rows
 // rows or fewer have none (the decode kernel takes them). The grid is an
-// upper bound on the total; workgroups past the last tile exit at once.
+// upper bound on the total; workgroups past the last tile exit at once. The
+// tiles are spread over the XCDs by their actual number, not the grid's:
+// workgroups go to the XCDs in turn, so the first `total` of them hold an
+// equal share on each (renumbered to one contiguous range per XCD), where
+// renumbering the whole grid would crowd the tiles onto the first XCDs.
+//
+// With tail_cus > 0 (the device's CU count), a last round of at most
+// tail_max tiles is left to grouped_tail_kernel: alone on their CUs those few
+// tiles would take a whole round's time while the other CUs idle.
+__device__ __forceinline__ int grouped_tail_tiles(int total, int tail_cus, int tail_max) {
+  if (tail_cus <= 0) return 0;
+  const int rem = total % tail_cus;
+  return rem <= tail_max ? rem : 0;
+}
+
 template <class G>
 __global__ __launch_bounds__(G::kThreads, 1) void grouped_gemm_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ sA, const uint8_t* __restrict__ B,
     const float* __restrict__ sB, uint16_t* __restrict__ C, const int32_t* __restrict__ offsets,
-    int E, int M_total, int N, int K, int min_rows) {
+    int E, int M_total, int N, int K, int min_rows, int tail_cus, int tail_max) {
   __shared__ __align__(16) uint8_t smem[G::kLdsBytes];
   const int tiles_n = (N + G::BN - 1) / G::BN;
-  const int pid = xcd_remap(blockIdx.x, gridDim.x);
+  const int all = total_units(offsets, E, M_total, G::BM, tiles_n, min_rows);
+  const int total = all - grouped_tail_tiles(all, tail_cus, tail_max);
+  if ((int)blockIdx.x >= total) return;
+  const int pid = xcd_remap(blockIdx.x, total);
   // the expert of tile pid (tiles numbered expert-major)
   const ExpertSlot es = locate_expert(offsets, E, M_total, pid, G::BM, tiles_n, min_rows);
   if (es.e < 0) return;
@@ -833,6 +859,44 @@ __global__ __launch_bounds__(G::kThreads, 1) void grouped_gemm_kernel(
   t.m0 = r0 + tm * G::BM; t.row_end = r1;
   t.n0 = tn * G::BN; t.N = N; t.K = K; t.ld = K;
   run_tile<G, 0>(t, smem);
+}
+
+// The tiles grouped_gemm_kernel<G> leaves over (the last `rem` of its
+// numbering, as it counts them), each computed as (G::BM / S::BM) x
+// (G::BN / S::BN) subtiles of the smaller shape S: a partial round of large
+// tiles becomes one round of small ones, spread over every CU. The subtiles
+// of one tile are consecutive on one XCD. The arithmetic per output is the
+// same as in the large tile (bit-identical).
+template <class G, class S>
+__global__ __launch_bounds__(S::kThreads, 1) void grouped_tail_kernel(
+    const uint8_t* __restrict__ A, const float* __restrict__ sA, const uint8_t* __restrict__ B,
+    const float* __restrict__ sB, uint16_t* __restrict__ C, const int32_t* __restrict__ offsets,
+    int E, int M_total, int N, int K, int tail_cus, int tail_max) {
+  static_assert(G::BM % S::BM == 0 && G::BN % S::BN == 0, "subtiles must divide the tile");
+  constexpr int kSubM = G::BM / S::BM, kSubN = G::BN / S::BN, kSubs = kSubM * kSubN;
+  __shared__ __align__(16) uint8_t smem[S::kLdsBytes];
+  const int tiles_n = (N + G::BN - 1) / G::BN;
+  const int all = total_units(offsets, E, M_total, G::BM, tiles_n, 0);
+  const int rem = grouped_tail_tiles(all, tail_cus, tail_max);
+  if ((int)blockIdx.x >= rem * kSubs) return;
+  const int sid = xcd_remap(blockIdx.x, rem * kSubs);
+  const int tile = all - rem + sid / kSubs, sub = sid % kSubs;
+  const ExpertSlot es = locate_expert(offsets, E, M_total, tile, G::BM, tiles_n, 0);
+  if (es.e < 0) return;
+  int tm, tn;
+  tile_coords(tile - es.base, (es.r1 - es.r0 + G::BM - 1) / G::BM, tiles_n, tm, tn);
+  const int m0 = es.r0 + tm * G::BM + (sub / kSubN) * S::BM;
+  const int n0 = tn * G::BN + (sub % kSubN) * S::BN;
+  if (m0 >= es.r1 || n0 >= N) return;     // a subtile past the expert's rows or the last columns
+  const int64_t nkb = K / BK;
+  Tile t;
+  t.A = A; t.sA = sA; t.sa_stride = M_total;
+  t.B = B + (int64_t)es.e * N * K;
+  t.sB = sB + (int64_t)es.e * (N / BK) * nkb;
+  t.C = C; t.Q = nullptr; t.sQ = nullptr; t.QT = nullptr; t.sQT = nullptr;
+  t.m0 = m0; t.row_end = es.r1;
+  t.n0 = n0; t.N = N; t.K = K; t.ld = K;
+  run_tile<S, 0>(t, smem);
 }
 
 // Per-expert Wgrad: C[e] = A_e B_e^T over expert e's tokens, row-mode scales.
@@ -917,13 +981,25 @@ int device_cus(hipStream_t stream) {
 // 4 us (its first loads and its epilogue), where a round is `per_cu` tiles:
 // as many workgroups as fit on a CU together (LDS and registers).
 struct TileEst {
-  int bm, bn, per_cu;
+  int bm, bn, depth, per_cu;
   double lat, thr;
 };
-enum DenseTile { kT256x256, kT256x224, kT224x256, kT128x256, kT128x128, kT64x64, kDenseTiles };
-constexpr TileEst kTileEst[kDenseTiles] = {{256, 256, 1, 80.0, 650.0}, {256, 224, 1, 70.0, 637.0},
-                                           {224, 256, 1, 70.0, 637.0}, {128, 256, 1, 54.0, 536.0},
-                                           {128, 128, 2, 43.0, 531.0}, {64, 64, 4, 33.0, 333.0}};
+enum DenseTile {
+  kT256x256, kT256x224, kT224x256, kT128x256, kT128x128, kT64x64, kT128x128d3, kT64x64d3, kDenseTiles
+};
+constexpr TileEst kTileEst[kDenseTiles] = {
+    {256, 256, 2, 1, 80.0, 650.0}, {256, 224, 3, 1, 70.0, 637.0}, {224, 256, 3, 1, 70.0, 637.0},
+    {128, 256, 2, 1, 54.0, 536.0}, {128, 128, 2, 2, 43.0, 531.0}, {64, 64, 2, 4, 33.0, 333.0},
+    {128, 128, 3, 1, 32.0, 499.0}, {64, 64, 3, 3, 23.0, 322.0}};
+template <class G>
+constexpr bool est_matches(DenseTile t) {
+  return kTileEst[t].bm == G::BM && kTileEst[t].bn == G::BN && kTileEst[t].depth == (G::DA > G::DB ? G::DA : G::DB);
+}
+static_assert(est_matches<Cfg256x256>(kT256x256) && est_matches<Cfg256x224>(kT256x224) &&
+                  est_matches<Cfg224x256>(kT224x256) && est_matches<Cfg128x256>(kT128x256) &&
+                  est_matches<Cfg128x128>(kT128x128) && est_matches<Cfg64x64>(kT64x64) &&
+                  est_matches<Cfg128x128d3>(kT128x128d3) && est_matches<Cfg64x64d3>(kT64x64d3),
+              "the estimate table follows the tile configurations");
 
 int pick_dense(int64_t M, int64_t N, int64_t K, hipStream_t stream) {
   const int cus = device_cus(stream);
@@ -1205,16 +1281,20 @@ hipError_t launch_gemm_blockscaled(const uint8_t* A, const float* sA, const uint
     case kT128x256: return launch_dense<Cfg128x256, 0>(A, sA, B, sB, row_mode, C, nullptr, nullptr, M, N, K, stream);
     case kT128x128: return launch_dense<Cfg128x128, 0>(A, sA, B, sB, row_mode, C, nullptr, nullptr, M, N, K, stream);
     case kT64x64: return launch_dense<Cfg64x64, 0>(A, sA, B, sB, row_mode, C, nullptr, nullptr, M, N, K, stream);
+    case kT128x128d3:
+      return launch_dense<Cfg128x128d3, 0>(A, sA, B, sB, row_mode, C, nullptr, nullptr, M, N, K, stream);
+    case kT64x64d3: return launch_dense<Cfg64x64d3, 0>(A, sA, B, sB, row_mode, C, nullptr, nullptr, M, N, K, stream);
     default: return launch_dense<Cfg256x256, 0>(A, sA, B, sB, row_mode, C, nullptr, nullptr, M, N, K, stream);
   }
 }
 
-void gemm_blockscaled_tile(int64_t M, int64_t N, int64_t K, int row_mode, int* bm, int* bn) {
+void gemm_blockscaled_tile(int64_t M, int64_t N, int64_t K, int row_mode, int* bm, int* bn, int* depth) {
   using namespace gemm;
   (void)row_mode;
   const int t = pick_dense(M, N, K, nullptr);
   *bm = kTileEst[t].bm;
   *bn = kTileEst[t].bn;
+  if (depth) *depth = kTileEst[t].depth;
 }
 
 hipError_t launch_gemm_blockscaled_pow2(const uint8_t* A, const float* sA, const uint8_t* B,
@@ -1264,9 +1344,20 @@ hipError_t launch_grouped_gemm_blockscaled(const uint8_t* A, const float* sA, co
   // tile kernel, costs more than the tile rounds it saves: 2,041 against
   // 1,966 us for the MoE up projection.)
   if (M_total > (int64_t)E * dec::kBM) {
+    // a last round that one round of the tail kernel's subtiles can hold
+    // (kTailPerCu of them per CU) goes to the tail kernel; the tail count is
+    // only known on the device, and with none the tail launch exits at once
+    using S = TailCfg;
+    constexpr int subs_per_tile = (G::BM / S::BM) * (G::BN / S::BN);
+    const int cus = device_cus(stream);
+    const int tail_max = cus * kTailPerCu / subs_per_tile;
     const int64_t tiles = ((M_total + G::BM - 1) / G::BM + E) * tiles_n;
     hipLaunchKernelGGL((grouped_gemm_kernel<G>), dim3((unsigned)tiles), dim3(G::kThreads), 0, stream, A, sA, B,
-                       sB, C, offsets, E, (int)M_total, (int)N, (int)K, 0);
+                       sB, C, offsets, E, (int)M_total, (int)N, (int)K, 0, cus, tail_max);
+    const hipError_t e0 = hipGetLastError();
+    if (e0 != hipSuccess || tail_max == 0) return e0;
+    hipLaunchKernelGGL((grouped_tail_kernel<G, S>), dim3((unsigned)(tail_max * subs_per_tile)), dim3(S::kThreads), 0,
+                       stream, A, sA, B, sB, C, offsets, E, (int)M_total, (int)N, (int)K, cus, tail_max);
     return hipGetLastError();
   }
   // Few rows per expert on average (decode): the weight-streaming kernel for
@@ -1284,7 +1375,7 @@ hipError_t launch_grouped_gemm_blockscaled(const uint8_t* A, const float* sA, co
   if (e1 != hipSuccess) return e1;
   const int64_t tiles = ((M_total + G::BM - 1) / G::BM + big) * tiles_n;
   hipLaunchKernelGGL((grouped_gemm_kernel<G>), dim3((unsigned)tiles), dim3(G::kThreads), 0, stream, A, sA, B, sB,
-                     C, offsets, E, (int)M_total, (int)N, (int)K, dec::kBM);
+                     C, offsets, E, (int)M_total, (int)N, (int)K, dec::kBM, 0, 0);
   return hipGetLastError();
 }
 

@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define FP8BS_ABI_VERSION 8
+#define FP8BS_ABI_VERSION 9
 
 #ifndef FP8BS_API
 #define FP8BS_API __attribute__((visibility("default")))
@@ -132,15 +132,18 @@ FP8BS_API int fp8_gemm_blockscaled(const uint8_t* A, const float* sA, const uint
                          int64_t M, int64_t N, int64_t K, void* stream);
 
 /*
- * The output tile fp8_gemm_blockscaled uses for an M x N x K problem in the
- * given scale mode on the current device: *bm rows by *bn columns per
- * workgroup (the kernel is chosen per shape so that the tiles fill whole
- * rounds of the device's compute units). A query only: it launches nothing.
+ * The kernel fp8_gemm_blockscaled uses for an M x N x K problem in the given
+ * scale mode on the current device: *bm rows by *bn columns of output per
+ * workgroup, and *depth, the K chunks its deeper operand ring holds (its
+ * loads run depth - 1 chunks ahead); depth may be NULL. The kernel is chosen
+ * per shape from an estimate of its time: large tiles that fill whole rounds
+ * of the device's compute units on large problems, smaller ones that spread a
+ * problem with few tiles over all of them. A query only: it launches nothing.
  * Returns FP8BS_ERR_NULL_PTR if bm or bn is NULL, FP8BS_ERR_MODE for an
  * unknown mode, FP8BS_ERR_SHAPE for sizes fp8_gemm_blockscaled rejects.
  */
 FP8BS_API int fp8_gemm_blockscaled_tile(int64_t M, int64_t N, int64_t K, int b_scale_mode,
-                         int* bm, int* bn);
+                         int* bm, int* bn, int* depth);
 
 /*
  * Power-of-two scale variant (report section 3.5.2 on the innerforce.co.kr

@@ -7,9 +7,10 @@
   one full output row per m-tile, the row's offset inside its tile moving
   from tile to tile, so every wave row and both halves of every tile are seen.
 * The grouped GEMM's tile kernel (chosen when the experts average more than
-  256 rows) on ragged experts that include empty ones, and skewed batches whose
-  few large experts go to the tile kernel while the rest take the
-  weight-streaming kernel.
+  256 rows) on ragged experts that include empty ones, with and without a
+  last partial round left to its 64x64-subtile tail kernel, and skewed
+  batches whose few large experts go to the tile kernel while the rest take
+  the weight-streaming kernel.
 * The MoE activation and expert-weight quantizers at their full sizes
   (65,536 x 7,168 and 65,536 x 2,048 activations, 32 x 4,096 x 7,168 and
   32 x 7,168 x 2,048 weights), bit for bit against the oracle.
@@ -54,14 +55,18 @@ def _check(C, ref, absref, what):
     return worst
 
 
-# shapes that pick each tile on a 256-CU MI355X; the test asserts the pick
-TILE_CASES = [((4096, 4096, 256), (256, 256)),
-              ((4096, 7168, 256), (256, 224)),
-              ((7168, 2048, 256), (224, 256)),
-              ((7168, 4096, 128), (224, 256)),
-              ((777, 5120, 128), (128, 256)),      # ragged last m-tile (9 rows)
-              ((1700, 2048, 128), (128, 128)),     # ragged last m-tile (36 rows)
-              ((300, 640, 256), (64, 64))]         # ragged last m-tile (44 rows)
+# shapes that pick each kernel (rows, columns, ring depth) on a 256-CU
+# MI355X; the test asserts the pick
+TILE_CASES = [((4096, 4096, 256), (256, 256, 2)),
+              ((4096, 7168, 256), (256, 224, 3)),
+              ((7168, 2048, 256), (224, 256, 3)),
+              ((7168, 4096, 128), (224, 256, 3)),
+              ((777, 5120, 128), (128, 256, 2)),      # ragged last m-tile (9 rows)
+              ((3700, 2176, 128), (128, 128, 2)),     # ragged last m-tile (116 rows)
+              ((1700, 2048, 128), (128, 128, 3)),     # ragged last m-tile (36 rows)
+              ((1300, 3072, 128), (64, 64, 2)),       # ragged last m-tile (20 rows)
+              ((300, 640, 256), (64, 64, 3)),         # ragged last m-tile (44 rows)
+              ((1, 128, 128), (64, 64, 3))]           # one row
 
 
 def test_tile_cases_cover_every_tile(dev):
@@ -87,7 +92,7 @@ def test_gemm_every_tile_full_output(dev, shape, tile, mode):
 
 def _rows_per_tile(M, N, K, mode):
     """One row per m-tile, at offset 16*(t mod BM/16) + (7t mod 16) inside tile t."""
-    bm, _ = fb.fp8_gemm_blockscaled_tile(M, N, K, mode)
+    bm = fb.fp8_gemm_blockscaled_tile(M, N, K, mode)[0]
     rows = [t * bm + (16 * (t % (bm // 16)) + (7 * t) % 16) % bm for t in range(-(-M // bm))]
     return np.array(sorted({min(r, M - 1) for r in rows} | {M - 1}))
 
@@ -174,6 +179,43 @@ def test_moe_expert_weight_quantizers_full_size(dev):
             assert_codes_equal(u8(q), qo, f"{key}[{e}] codes")
             assert_scales_equal(s.cpu().numpy(), so, f"{key}[{e}] scales")
         del W
+
+
+def _grouped_route(counts, N, cus):
+    """(tiles of the grouped tile kernel, tiles left to its tail kernel): a
+    last round of 256x256 tiles that fits one round of 64x64 subtiles, three
+    per CU, goes to the tail."""
+    tiles = sum(-(-c // 256) for c in counts) * -(-N // 256)
+    rem = tiles % cus
+    tail = rem if rem * 16 <= 3 * cus else 0
+    return tiles - tail, tail
+
+
+@pytest.mark.parametrize("counts,N,K,route", [
+    ([7580] * 9 + [0] + [7600], 256, 128, (256, 44)),       # one full round, 44 tiles left to the tail
+    ([0, 900, 0, 250], 512, 256, (0, 10)),                  # fewer tiles than a quarter of the CUs: all tail
+    ([5000, 5000, 0, 1], 1280, 128, (205, 0)),             # a partial round of 205 tiles: no tail
+    ([16367, 16384, 16384, 16379], 512, 128, (512, 0)),     # exactly two rounds
+    ([38909, 38912], 256, 128, (256, 48)),                  # the largest tail: 768 subtiles, 3 per CU
+    ([38909, 38913], 256, 128, (305, 0)),                   # one tile more: no tail
+])
+def test_grouped_tile_kernel_and_its_tail(dev, counts, N, K, route):
+    off = np.zeros(len(counts) + 1, np.int32)
+    off[1:] = np.cumsum(counts)
+    M, E = int(off[-1]), len(counts)
+    assert M > 256 * E, "the case must take the grouped tile kernel"
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    if cus == 256:
+        assert _grouped_route(counts, N, cus) == route
+    seed = 5 * M + N
+    A, sA = _codes((M, K), seed), _scales((K // 128, M), seed + 1)
+    B, sB = _codes((E, N, K), seed + 2), _scales((E, N // 128, K // 128), seed + 3)
+    C = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=dev)
+    fb.fp8_grouped_gemm_blockscaled(A.to(dev), sA.to(dev), B.to(dev), sB.to(dev), torch.from_numpy(off).to(dev),
+                                    out=C)
+    ref, absref = oracle.grouped_gemm_ref(A.numpy(), sA.numpy(), B.numpy(), sB.numpy(), off)
+    torch.cuda.synchronize()
+    _check(C, ref, absref, f"grouped {counts[:4]}... N={N} K={K} route {route}")
 
 
 @pytest.mark.parametrize("counts,N,K", [
