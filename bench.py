@@ -27,6 +27,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -41,11 +42,21 @@ KERNEL_SOURCES = [os.path.join(ROOT, "fp8_block_scaled_x1_amd", "csrc", f)
                   for f in ("gemm.hip", "quant.hip", "moe.hip", "device_common.h")]
 
 
+def _code_only(text):
+    """Kernel source without its comments and with whitespace collapsed (the
+    sources hold no string literal with a comment marker)."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_digest():
+    """Digest of the kernel sources' code: it changes when the code does, not
+    when only comments do."""
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        with open(p, "rb") as f:
-            h.update(f.read())
+        with open(p, encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

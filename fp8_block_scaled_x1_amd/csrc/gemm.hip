@@ -16,10 +16,10 @@
 // the next subtile.
 //
 // Structure (one BM x BN output tile per workgroup of 8 waves; 4 for the
-// hardware-scaled variant's 256x256 tiles):
+// 64x64 tiles and the hardware-scaled variant's 256x256 tiles):
 //   * one pipeline stage = one K chunk: A[BM][128] + B[BN][128] bytes plus the
 //     chunk's scale vectors, moved L2 -> LDS with direct-to-LDS loads (no VGPR
-//     staging); two stages; one barrier per chunk;
+//     staging); two or three stages per operand; one barrier per chunk;
 //   * every direct-to-LDS load instruction reads 8 whole 128-byte rows (full
 //     cache lines); inside LDS the 16-byte column of row r is XOR-swizzled with
 //     (r & 7) ^ ((r >> 3) & 1), which keeps the MFMA fragment reads free of
@@ -38,9 +38,13 @@
 //   * workgroup -> tile mapping is XCD-aware: consecutive tiles in a grouped
 //     (8 m-tiles wide) order land on the same XCD, so the A and B panels they
 //     share stay in that XCD's L2;
-//   * the tile shape is chosen on the host per problem so that the number of
-//     tiles fills whole rounds of the 256 CUs where possible.
+//   * the kernel (tile shape and ring depth) is chosen on the host per problem
+//     from an estimate of its time: large tiles in whole rounds of the CUs for
+//     large problems, small ones spread over all CUs for problems with few
+//     tiles; the grouped GEMM leaves a short last round to a second launch of
+//     small subtiles.
 
+#include <algorithm>
 #include <atomic>
 #include <type_traits>
 

@@ -91,3 +91,10 @@ def test_clock_summary_drops_the_stale_leading_readings():
     s = bench.clock_summary([2079.0] * 5)          # no refresh seen: every reading kept
     assert s["median_mhz"] == 2079.0 and s["samples"] == 5 and s["stale_dropped"] == 0
     assert bench.clock_summary([]) is None
+
+
+def test_source_digest_ignores_comments_only():
+    code = "int f(int x) {\n  return x + 1;  // one more\n}\n/* block\n comment */\n"
+    assert bench._code_only(code) == bench._code_only(code.replace("one more", "plus one").replace("block", "b"))
+    assert bench._code_only(code) != bench._code_only(code.replace("x + 1", "x + 2"))
+    assert bench._code_only("a  =\n b;") == "a = b;"
