@@ -150,3 +150,48 @@ def test_graph_moe_dispatch_gemm_combine(dev):
         step(x, ids, w, eager, torch.cuda.current_stream().cuda_stream)
         torch.cuda.synchronize()
         assert _same(eager["out"], refs[(i + 1) % 3]["out"])
+
+
+def test_graph_grouped_gemm_tile_and_tail_routes(dev):
+    # the grouped GEMM's tile kernel and its tail launch decide on the device,
+    # from the offsets, which tiles the tail takes: one captured graph must
+    # follow offsets that change between replays (on 256 CUs: a round of 256
+    # tiles and a tail of 32, for two expert splits; a round and a tail of 8;
+    # no tail, with 80 tiles past the round left to the tile kernel)
+    E, M, N, K = 4, 2800, 6144, 256
+    routes = [[700, 700, 700, 700], [2800, 0, 0, 0], [1, 1, 1, 2797], [900, 900, 500, 500]]
+    g = torch.Generator(device=dev).manual_seed(5)
+    A = torch.randint(0, 256, (M, K), generator=g, device=dev, dtype=torch.int32).to(torch.uint8)
+    A[(A & 0x7F) == 0x7F] = 0x3B
+    B = torch.randint(0, 256, (E, N, K), generator=g, device=dev, dtype=torch.int32).to(torch.uint8)
+    B[(B & 0x7F) == 0x7F] = 0x3B
+    sA = 1e-2 + torch.rand((K // 128, M), generator=g, device=dev)
+    sB = 1e-2 + torch.rand((E, N // 128, K // 128), generator=g, device=dev)
+    offs = [torch.from_numpy(np.concatenate([[0], np.cumsum(c)]).astype(np.int32)).to(dev) for c in routes]
+    L = fb.lib()
+
+    def gemm(off, C, stream):
+        assert L.fp8_grouped_gemm_blockscaled(A.data_ptr(), sA.data_ptr(), B.data_ptr(), sB.data_ptr(), C.data_ptr(),
+                                              off.data_ptr(), E, M, N, K, stream) == 0
+
+    refs = []
+    for off in offs:
+        C = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        gemm(off, C, torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        refs.append(C)
+    off_g = offs[0].clone()
+    C_g = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    graph = _capture(lambda stream: gemm(off_g, C_g, stream))
+    for rep in range(8):
+        i = (3 * rep + 1) % len(routes)
+        off_g.copy_(offs[i])
+        C_g.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert _same(C_g, refs[i]), f"replay {rep}: route {routes[i]} differs from the eager result"
+        C = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        gemm(offs[(i + 1) % len(routes)], C, torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        assert _same(C, refs[(i + 1) % len(routes)])
