@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libfp8bs.so")
 
 F32, BF16 = 0, 1
 SCALE_BLOCK128, SCALE_ROW = 0, 1
-ABI_VERSION = 9
+ABI_VERSION = 10
 
 _c_int64 = ctypes.c_int64
 _vp = ctypes.c_void_p
@@ -28,7 +28,8 @@ _SIGNATURES = {
     "fp8_quant_act_128x1_T": [_vp, ctypes.c_int, _c_int64, _c_int64, _vp, _vp, _vp],
     "fp8_gemm_blockscaled": [_vp, _vp, _vp, _vp, ctypes.c_int, _vp, _c_int64, _c_int64, _c_int64, _vp],
     "fp8_gemm_blockscaled_tile": [_c_int64, _c_int64, _c_int64, ctypes.c_int, ctypes.POINTER(ctypes.c_int),
-                                  ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int)],
+                                  ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int),
+                                  ctypes.POINTER(ctypes.c_int)],
     "fp8_quant_act_1x128_pow2": [_vp, ctypes.c_int, _c_int64, _c_int64, _vp, _vp, _vp],
     "fp8_quant_w_128x128_pow2": [_vp, ctypes.c_int, _c_int64, _c_int64, _vp, _vp, _vp, _vp, _vp],
     "fp8_quant_act_128x1_T_pow2": [_vp, ctypes.c_int, _c_int64, _c_int64, _vp, _vp, _vp],
@@ -191,12 +192,12 @@ def fp8_gemm_blockscaled(A, sA, B, sB, b_scale_mode=SCALE_BLOCK128, out=None, po
 
 
 def fp8_gemm_blockscaled_tile(M, N, K, b_scale_mode=SCALE_BLOCK128):
-    """(rows, columns, ring depth) of the kernel fp8_gemm_blockscaled uses for this shape."""
-    bm, bn, depth = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    """(rows, columns, ring depth, tail tiles) of the kernel fp8_gemm_blockscaled uses for this shape."""
+    bm, bn, depth, tail = ctypes.c_int(), ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
     _check("fp8_gemm_blockscaled_tile",
            lib().fp8_gemm_blockscaled_tile(M, N, K, int(b_scale_mode), ctypes.byref(bm), ctypes.byref(bn),
-                                           ctypes.byref(depth)))
-    return bm.value, bn.value, depth.value
+                                           ctypes.byref(depth), ctypes.byref(tail)))
+    return bm.value, bn.value, depth.value, tail.value
 
 
 def fp8_gemm_blockscaled_q1x128(A, sA, B, sB, b_scale_mode=SCALE_BLOCK128):

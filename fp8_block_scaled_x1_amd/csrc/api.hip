@@ -133,11 +133,12 @@ int fp8_gemm_blockscaled(const uint8_t* A, const float* sA, const uint8_t* B, co
   return gemm_blockscaled(A, sA, B, sB, b_scale_mode, C, M, N, K, false, stream);
 }
 
-int fp8_gemm_blockscaled_tile(int64_t M, int64_t N, int64_t K, int b_scale_mode, int* bm, int* bn, int* depth) {
+int fp8_gemm_blockscaled_tile(int64_t M, int64_t N, int64_t K, int b_scale_mode, int* bm, int* bn, int* depth,
+                              int* tail_tiles) {
   if (!bm || !bn) return FP8BS_ERR_NULL_PTR;
   if (b_scale_mode != FP8BS_SCALE_BLOCK128 && b_scale_mode != FP8BS_SCALE_ROW) return FP8BS_ERR_MODE;
   if (M < 0 || N < 0 || K <= 0 || K % kG || N % kG) return FP8BS_ERR_SHAPE;
-  fp8bs::gemm_blockscaled_tile(M, N, K, b_scale_mode, bm, bn, depth);
+  fp8bs::gemm_blockscaled_tile(M, N, K, b_scale_mode, bm, bn, depth, tail_tiles);
   return FP8BS_OK;
 }
 

@@ -106,7 +106,8 @@ using Cfg64x64 = Cfg<64, 64, 2, 2, 2, 2>;
 // co-residency (128x128: one workgroup per CU; 64x64: three)
 using Cfg128x128d3 = Cfg<128, 128, 4, 2, 3, 3>;
 using Cfg64x64d3 = Cfg<64, 64, 2, 2, 3, 3>;
-// Subtiles of the grouped GEMM's tail kernel, and how many of its workgroups
+// Subtiles of the tail launches (a last partial round of 256x256 tiles, dense
+// or grouped, recomputed over every CU), and how many of their workgroups
 // share a CU (LDS and registers)
 using TailCfg = Cfg64x64d3;
 constexpr int kTailPerCu = 3;
@@ -903,6 +904,34 @@ __global__ __launch_bounds__(S::kThreads, 1) void grouped_tail_kernel(
   run_tile<S, 0>(t, smem);
 }
 
+// The last gridDim.x / subtiles-per-tile tiles of gemm_kernel<G>'s numbering,
+// from tile `first` on (that kernel's grid then covers only the tiles before
+// it), each computed as (G::BM / S::BM) x (G::BN / S::BN) subtiles of the
+// smaller shape S, spread over every CU. The subtiles of one tile are
+// consecutive on one XCD; the arithmetic per output is the large tile's.
+template <class G, class S, int ROW_MODE>
+__global__ __launch_bounds__(S::kThreads, 1) void dense_tail_kernel(
+    const uint8_t* __restrict__ A, const float* __restrict__ sA, const uint8_t* __restrict__ B,
+    const float* __restrict__ sB, uint16_t* __restrict__ C, int M, int N, int K, int first) {
+  static_assert(G::BM % S::BM == 0 && G::BN % S::BN == 0, "subtiles must divide the tile");
+  constexpr int kSubN = G::BN / S::BN, kSubs = (G::BM / S::BM) * kSubN;
+  __shared__ __align__(16) uint8_t smem[S::kLdsBytes];
+  const int tiles_m = (M + G::BM - 1) / G::BM, tiles_n = (N + G::BN - 1) / G::BN;
+  const int sid = xcd_remap(blockIdx.x, gridDim.x);
+  const int tile = first + sid / kSubs, sub = sid % kSubs;
+  int tm, tn;
+  tile_coords(tile, tiles_m, tiles_n, tm, tn, kGroupMDense);
+  const int m0 = tm * G::BM + (sub / kSubN) * S::BM;
+  const int n0 = tn * G::BN + (sub % kSubN) * S::BN;
+  if (m0 >= M || n0 >= N) return;     // a subtile past the last rows or columns
+  Tile t;
+  t.A = A; t.sA = sA; t.sa_stride = M;
+  t.B = B; t.sB = sB; t.C = C; t.Q = nullptr; t.sQ = nullptr; t.QT = nullptr; t.sQT = nullptr;
+  t.m0 = m0; t.row_end = M;
+  t.n0 = n0; t.N = N; t.K = K; t.ld = K;
+  run_tile<S, ROW_MODE>(t, smem);
+}
+
 // Per-expert Wgrad: C[e] = A_e B_e^T over expert e's tokens, row-mode scales.
 // A[N][ld] and B[K][ld] are the 128x1 transposed codes of the two operands
 // with every expert's tokens padded to whole 128-token groups: expert e's
@@ -1005,23 +1034,47 @@ static_assert(est_matches<Cfg256x256>(kT256x256) && est_matches<Cfg256x224>(kT25
                   est_matches<Cfg128x128d3>(kT128x128d3) && est_matches<Cfg64x64d3>(kT64x64d3),
               "the estimate table follows the tile configurations");
 
-int pick_dense(int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+static_assert(est_matches<TailCfg>(kT64x64d3), "the tail subtiles are the three-deep 64x64 kernel");
+
+// Estimated time (us) of `tiles` tiles of kernel c on `cus` CUs, K = k * 7168.
+double tile_estimate(const TileEst& c, int64_t tiles, int cus, double k) {
+  const int64_t per_cu = (tiles + cus - 1) / cus;
+  const int64_t rounds = (per_cu + c.per_cu - 1) / c.per_cu;
+  return std::max(c.lat * k, (double)per_cu * c.bm * c.bn / c.thr * k) + 4.0 * (double)rounds;
+}
+
+// The dense GEMM's choice: a kernel of kTileEst and, with 256x256 tiles, how
+// many of its last tiles a second launch computes as TailCfg subtiles.
+struct DensePick {
+  int tile;
+  int tail;
+};
+
+DensePick pick_dense(int64_t M, int64_t N, int64_t K, hipStream_t stream) {
   const int cus = device_cus(stream);
   const double k = (double)K / 7168.0;
   int best = 0;
   double best_t = 0.0;
   for (int i = 0; i < kDenseTiles; ++i) {
     const TileEst& c = kTileEst[i];
-    const int64_t tiles = ((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
-    const int64_t per_cu = (tiles + cus - 1) / cus;
-    const int64_t rounds = (per_cu + c.per_cu - 1) / c.per_cu;
-    const double t = std::max(c.lat * k, (double)per_cu * c.bm * c.bn / c.thr * k) + 4.0 * (double)rounds;
+    const double t = tile_estimate(c, ((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn), cus, k);
     if (i == 0 || t < best_t) {
       best = i;
       best_t = t;
     }
   }
-  return best;
+  // 256x256 tiles in whole rounds, and a last partial round that one round of
+  // subtiles holds (kTailPerCu per CU) as subtiles over every CU, launched
+  // behind them (about 2 us between the launches)
+  constexpr int subs = (Cfg256x256::BM / TailCfg::BM) * (Cfg256x256::BN / TailCfg::BN);
+  const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  const int64_t tail = tiles % cus, full = tiles - tail;
+  if (full > 0 && tail > 0 && tail * subs <= (int64_t)cus * kTailPerCu) {
+    const double t = tile_estimate(kTileEst[kT256x256], full, cus, k) +
+                     tile_estimate(kTileEst[kT64x64d3], tail * subs, cus, k) + 2.0;
+    if (t < best_t) return {kT256x256, (int)tail};
+  }
+  return {best, 0};
 }
 
 template <class G, int QOUT, int HW = 0>
@@ -1036,6 +1089,27 @@ hipError_t launch_dense(const uint8_t* A, const float* sA, const uint8_t* B, con
     hipLaunchKernelGGL((gemm_kernel<G, 0, QOUT, HW>), dim3(tiles), dim3(G::kThreads), 0, stream, A, sA, B, sB,
                        C, Q, sQ, QT, sQT, (int)M, (int)N, (int)K);
   return hipGetLastError();
+}
+
+// gemm_kernel<G> over all but the last `tail` tiles, then dense_tail_kernel
+// over those (BF16 output).
+template <class G, class S>
+hipError_t launch_dense_tail(const uint8_t* A, const float* sA, const uint8_t* B, const float* sB, int row_mode,
+                             uint16_t* C, int64_t M, int64_t N, int64_t K, int tail, hipStream_t stream) {
+  constexpr int subs = (G::BM / S::BM) * (G::BN / S::BN);
+  const int tiles = (int)(((M + G::BM - 1) / G::BM) * ((N + G::BN - 1) / G::BN));
+  const int full = tiles - tail;
+  auto go = [&](auto rm) {
+    constexpr int R = decltype(rm)::value;
+    hipLaunchKernelGGL((gemm_kernel<G, R, 0, 0>), dim3(full), dim3(G::kThreads), 0, stream, A, sA, B, sB, C, nullptr,
+                       nullptr, nullptr, nullptr, (int)M, (int)N, (int)K);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((dense_tail_kernel<G, S, R>), dim3(tail * subs), dim3(S::kThreads), 0, stream, A, sA, B, sB,
+                       C, (int)M, (int)N, (int)K, full);
+    return hipGetLastError();
+  };
+  return row_mode ? go(std::integral_constant<int, 1>{}) : go(std::integral_constant<int, 0>{});
 }
 
 // ---------------------------------------------------------------------------
@@ -1279,7 +1353,10 @@ hipError_t launch_gemm_blockscaled(const uint8_t* A, const float* sA, const uint
                                    const float* sB, int row_mode, uint16_t* C, int64_t M,
                                    int64_t N, int64_t K, hipStream_t stream) {
   using namespace gemm;
-  switch (pick_dense(M, N, K, stream)) {
+  const DensePick p = pick_dense(M, N, K, stream);
+  if (p.tail > 0)
+    return launch_dense_tail<Cfg256x256, TailCfg>(A, sA, B, sB, row_mode, C, M, N, K, p.tail, stream);
+  switch (p.tile) {
     case kT256x224: return launch_dense<Cfg256x224, 0>(A, sA, B, sB, row_mode, C, nullptr, nullptr, M, N, K, stream);
     case kT224x256: return launch_dense<Cfg224x256, 0>(A, sA, B, sB, row_mode, C, nullptr, nullptr, M, N, K, stream);
     case kT128x256: return launch_dense<Cfg128x256, 0>(A, sA, B, sB, row_mode, C, nullptr, nullptr, M, N, K, stream);
@@ -1292,13 +1369,15 @@ hipError_t launch_gemm_blockscaled(const uint8_t* A, const float* sA, const uint
   }
 }
 
-void gemm_blockscaled_tile(int64_t M, int64_t N, int64_t K, int row_mode, int* bm, int* bn, int* depth) {
+void gemm_blockscaled_tile(int64_t M, int64_t N, int64_t K, int row_mode, int* bm, int* bn, int* depth,
+                           int* tail) {
   using namespace gemm;
   (void)row_mode;
-  const int t = pick_dense(M, N, K, nullptr);
-  *bm = kTileEst[t].bm;
-  *bn = kTileEst[t].bn;
-  if (depth) *depth = kTileEst[t].depth;
+  const DensePick p = pick_dense(M, N, K, nullptr);
+  *bm = kTileEst[p.tile].bm;
+  *bn = kTileEst[p.tile].bn;
+  if (depth) *depth = kTileEst[p.tile].depth;
+  if (tail) *tail = p.tail;
 }
 
 hipError_t launch_gemm_blockscaled_pow2(const uint8_t* A, const float* sA, const uint8_t* B,

@@ -18,7 +18,8 @@ hipError_t launch_gemm_blockscaled(const uint8_t* A, const float* sA, const uint
                                    const float* sB, int row_mode, uint16_t* C, int64_t M,
                                    int64_t N, int64_t K, hipStream_t stream);
 // the output tile (rows, columns) launch_gemm_blockscaled picks for a shape
-void gemm_blockscaled_tile(int64_t M, int64_t N, int64_t K, int row_mode, int* bm, int* bn, int* depth);
+void gemm_blockscaled_tile(int64_t M, int64_t N, int64_t K, int row_mode, int* bm, int* bn, int* depth,
+                           int* tail);
 // sA and sB hold powers of two; the MFMA applies them as E8M0 block scales
 hipError_t launch_gemm_blockscaled_pow2(const uint8_t* A, const float* sA, const uint8_t* B,
                                         const float* sB, int row_mode, uint16_t* C, int64_t M,

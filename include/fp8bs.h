@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define FP8BS_ABI_VERSION 9
+#define FP8BS_ABI_VERSION 10
 
 #ifndef FP8BS_API
 #define FP8BS_API __attribute__((visibility("default")))
@@ -134,16 +134,19 @@ FP8BS_API int fp8_gemm_blockscaled(const uint8_t* A, const float* sA, const uint
 /*
  * The kernel fp8_gemm_blockscaled uses for an M x N x K problem in the given
  * scale mode on the current device: *bm rows by *bn columns of output per
- * workgroup, and *depth, the K chunks its deeper operand ring holds (its
- * loads run depth - 1 chunks ahead); depth may be NULL. The kernel is chosen
- * per shape from an estimate of its time: large tiles that fill whole rounds
- * of the device's compute units on large problems, smaller ones that spread a
- * problem with few tiles over all of them. A query only: it launches nothing.
- * Returns FP8BS_ERR_NULL_PTR if bm or bn is NULL, FP8BS_ERR_MODE for an
- * unknown mode, FP8BS_ERR_SHAPE for sizes fp8_gemm_blockscaled rejects.
+ * workgroup; *depth, the K chunks its deeper operand ring holds (its loads
+ * run depth - 1 chunks ahead); *tail_tiles, how many of its last tiles a
+ * second launch computes as 64 x 64 subtiles spread over every compute unit
+ * (0: none). The kernel is chosen per shape from an estimate of its time:
+ * large tiles in whole rounds of the device's compute units on large
+ * problems, with a short last round as subtiles, smaller tiles spread over
+ * all units for problems with few tiles. depth and tail_tiles may be NULL.
+ * A query only: it launches nothing. Returns FP8BS_ERR_NULL_PTR if bm or bn
+ * is NULL, FP8BS_ERR_MODE for an unknown mode, FP8BS_ERR_SHAPE for sizes
+ * fp8_gemm_blockscaled rejects.
  */
 FP8BS_API int fp8_gemm_blockscaled_tile(int64_t M, int64_t N, int64_t K, int b_scale_mode,
-                         int* bm, int* bn, int* depth);
+                         int* bm, int* bn, int* depth, int* tail_tiles);
 
 /*
  * Power-of-two scale variant (report section 3.5.2 on the innerforce.co.kr

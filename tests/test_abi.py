@@ -47,7 +47,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.fp8bs_abi_version() == fb.ABI_VERSION == 9
+    assert L.fp8bs_abi_version() == fb.ABI_VERSION == 10
     for code in range(-8, 1):
         assert fb.status_string(code) not in ("", "unknown status")
     assert fb.status_string(-99) == "unknown status"
@@ -205,13 +205,14 @@ def test_binding_rejects_wrong_output_shapes(L):
 
 def test_tile_query_validation(L):
     import ctypes
-    bm, bn, d = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    bm, bn, d, t = ctypes.c_int(), ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
     q = L.fp8_gemm_blockscaled_tile
-    assert q(4096, 7168, 7168, 2, ctypes.byref(bm), ctypes.byref(bn), ctypes.byref(d)) == -5
-    assert q(4096, 7100, 7168, 0, ctypes.byref(bm), ctypes.byref(bn), ctypes.byref(d)) == -2
-    assert q(4096, 7168, 7100, 1, ctypes.byref(bm), ctypes.byref(bn), ctypes.byref(d)) == -2
-    assert q(4096, 7168, 7168, 0, None, ctypes.byref(bn), ctypes.byref(d)) == -1
-    assert q(4096, 7168, 7168, 0, ctypes.byref(bm), ctypes.byref(bn), None) == 0      # depth is optional
+    outs = (ctypes.byref(bm), ctypes.byref(bn), ctypes.byref(d), ctypes.byref(t))
+    assert q(4096, 7168, 7168, 2, *outs) == -5
+    assert q(4096, 7100, 7168, 0, *outs) == -2
+    assert q(4096, 7168, 7100, 1, *outs) == -2
+    assert q(4096, 7168, 7168, 0, None, ctypes.byref(bn), ctypes.byref(d), ctypes.byref(t)) == -1
+    assert q(4096, 7168, 7168, 0, ctypes.byref(bm), ctypes.byref(bn), None, None) == 0   # depth, tail optional
     assert (bm.value, bn.value) == (256, 224)
 
 
@@ -234,19 +235,23 @@ def test_tile_query_follows_the_shape(L):
     # device answers): skinny problems take the small tiles that spread them
     # over every CU, full-size layers the large ones
     import ctypes
-    bm, bn, d = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    bm, bn, d, t = ctypes.c_int(), ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
 
     def tile(M, N, K):
-        assert L.fp8_gemm_blockscaled_tile(M, N, K, 0, ctypes.byref(bm), ctypes.byref(bn), ctypes.byref(d)) == 0
-        return bm.value, bn.value, d.value
+        assert L.fp8_gemm_blockscaled_tile(M, N, K, 0, ctypes.byref(bm), ctypes.byref(bn), ctypes.byref(d),
+                                           ctypes.byref(t)) == 0
+        return bm.value, bn.value, d.value, t.value
 
     # a few tokens: 112 tiles of 256 rows would idle 144 CUs; one small tile
     # per CU, alone there, with its loads two chunks ahead
-    assert tile(64, 7168, 7168) == (64, 64, 3)
-    assert tile(512, 7168, 7168) == (128, 128, 3)
-    assert tile(1024, 7168, 7168) == (128, 256, 2)
-    assert tile(4096, 2048, 7168) == (128, 256, 2)
-    assert tile(4096, 7168, 7168) == (256, 224, 3)     # 512 tiles: two full rounds
-    assert tile(4096, 4096, 4096) == (256, 256, 2)
-    assert tile(7168, 4096, 4096) == (224, 256, 3)
-    assert tile(1, 128, 128) == (64, 64, 3)
+    assert tile(64, 7168, 7168) == (64, 64, 3, 0)
+    assert tile(512, 7168, 7168) == (128, 128, 3, 0)
+    assert tile(1024, 7168, 7168) == (128, 256, 2, 0)
+    assert tile(4096, 2048, 7168) == (128, 256, 2, 0)
+    assert tile(4096, 7168, 7168) == (256, 224, 3, 0)     # 512 tiles: two full rounds
+    assert tile(4096, 4096, 4096) == (256, 256, 2, 0)
+    assert tile(7168, 4096, 4096) == (224, 256, 3, 0)
+    assert tile(1, 128, 128) == (64, 64, 3, 0)
+    # 784 tiles of 256x256: three rounds, and the 16 left as 256 subtiles of 64x64
+    assert tile(7168, 7168, 4096) == (256, 256, 2, 16)
+    assert tile(5120, 7168, 7168) == (256, 256, 2, 48)

@@ -2,7 +2,8 @@
 
 * Every output tile the host can choose for fp8_gemm_blockscaled is run at a
   shape that picks it (confirmed through fp8_gemm_blockscaled_tile), in both
-  scale modes, and the whole NaN-prefilled output is compared with the oracle.
+  scale modes, and the whole NaN-prefilled output is compared with the oracle;
+  so is the region a tail launch of 64x64 subtiles computes.
 * The dense Fprop, Dgrad and Wgrad layers at their real sizes are compared on
   one full output row per m-tile, the row's offset inside its tile moving
   from tile to tile, so every wave row and both halves of every tile are seen.
@@ -55,18 +56,18 @@ def _check(C, ref, absref, what):
     return worst
 
 
-# shapes that pick each kernel (rows, columns, ring depth) on a 256-CU
-# MI355X; the test asserts the pick
-TILE_CASES = [((4096, 4096, 256), (256, 256, 2)),
-              ((4096, 7168, 256), (256, 224, 3)),
-              ((7168, 2048, 256), (224, 256, 3)),
-              ((7168, 4096, 128), (224, 256, 3)),
-              ((777, 5120, 128), (128, 256, 2)),      # ragged last m-tile (9 rows)
-              ((3700, 2176, 128), (128, 128, 2)),     # ragged last m-tile (116 rows)
-              ((1700, 2048, 128), (128, 128, 3)),     # ragged last m-tile (36 rows)
-              ((1300, 3072, 128), (64, 64, 2)),       # ragged last m-tile (20 rows)
-              ((300, 640, 256), (64, 64, 3)),         # ragged last m-tile (44 rows)
-              ((1, 128, 128), (64, 64, 3))]           # one row
+# shapes that pick each kernel (rows, columns, ring depth, tail tiles) on a
+# 256-CU MI355X; the test asserts the pick
+TILE_CASES = [((4096, 4096, 256), (256, 256, 2, 0)),
+              ((4096, 7168, 256), (256, 224, 3, 0)),
+              ((7168, 2048, 256), (224, 256, 3, 0)),
+              ((7168, 4096, 128), (224, 256, 3, 0)),
+              ((777, 5120, 128), (128, 256, 2, 0)),      # ragged last m-tile (9 rows)
+              ((3700, 2176, 128), (128, 128, 2, 0)),     # ragged last m-tile (116 rows)
+              ((1700, 2048, 128), (128, 128, 3, 0)),     # ragged last m-tile (36 rows)
+              ((1300, 3072, 128), (64, 64, 2, 0)),       # ragged last m-tile (20 rows)
+              ((300, 640, 256), (64, 64, 3, 0)),         # ragged last m-tile (44 rows)
+              ((1, 128, 128), (64, 64, 3, 0))]           # one row
 
 
 def test_tile_cases_cover_every_tile(dev):
@@ -88,6 +89,27 @@ def test_gemm_every_tile_full_output(dev, shape, tile, mode):
     ref, absref = oracle.gemm_ref(A.numpy(), sA.numpy(), B.numpy(), sB.numpy(), mode)
     torch.cuda.synchronize()
     _check(C, ref, absref, f"gemm {M}x{N}x{K} tile {tile} mode {mode}")
+
+
+@pytest.mark.parametrize("shape", [(4352, 4096, 2048), (4252, 3968, 2048)])
+@pytest.mark.parametrize("mode", [MODE_BLOCK, MODE_ROW])
+def test_gemm_tail_launch(dev, shape, mode):
+    # 17 x 16 tiles of 256x256: one round of 256 and 16 left to the tail
+    # launch as 64x64 subtiles. The tile order takes 4 m-tiles at a time, so
+    # the last 16 tiles are the 16 n-tiles of the 17th m-tile: every row from
+    # 4096 on is checked in full (the second shape has a ragged last m-tile
+    # and a last n-tile of 128 columns), with one row of every other m-tile.
+    M, N, K = shape
+    assert fb.fp8_gemm_blockscaled_tile(M, N, K, mode) == (256, 256, 2, 16)
+    A, B = _codes((M, K), M + N + mode), _codes((N, K), 5 * N + mode)
+    sA = _scales((K // 128, M), 23 + M)
+    sB = _scales((N // 128, K // 128) if mode == MODE_BLOCK else (K // 128, N), 29 + N)
+    C = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=dev)
+    fb.fp8_gemm_blockscaled(A.to(dev), sA.to(dev), B.to(dev), sB.to(dev), mode, out=C)
+    rows = np.array(sorted(set(range(4096, M)) | {t * 256 + (37 * t) % 256 for t in range(16)}))
+    ref, absref = oracle.gemm_ref_rows(A[rows].numpy(), sA[:, rows].numpy(), B.numpy(), sB.numpy(), mode)
+    torch.cuda.synchronize()
+    _check(C[rows], ref, absref, f"gemm {M}x{N}x{K} with a tail, mode {mode}")
 
 
 def _rows_per_tile(M, N, K, mode):
