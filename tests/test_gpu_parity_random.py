@@ -3,7 +3,9 @@ against the oracle, beyond the hand-picked cases of the other files.
 
 * Dense GEMM: M in 1..1199, N and K multiples of 128 up to 1,536, both scale
   modes, codes over the whole E4M3 range, scales spread over 2^-8 .. 2^8;
-  the whole NaN-prefilled output is checked.
+  the whole NaN-prefilled output is checked. Larger shapes whose last round
+  of 256x256 tiles goes to the tail launch, checked on rows spread over the
+  tail's tiles and over every other m-tile.
 * Grouped GEMM: 1..16 experts whose row counts mix empty, small (<= 32),
   medium and past-one-pass (> 256) experts, so both the weight-streaming and
   the tile kernel run, alone and together; the whole output is checked.
@@ -66,6 +68,50 @@ def test_random_dense_gemm(dev, seed):
     ref, absref = oracle.gemm_ref(A, sA, B, sB, mode)
     torch.cuda.synchronize()
     _check(C, ref, absref, f"seed {seed}: gemm {M}x{N}x{K} mode {mode}")
+
+
+def _tail_m_tiles(tiles_m, tiles_n, tail, group_m=4):
+    """m-tiles holding the dense GEMM's last `tail` tiles: its tile order takes
+    group_m m-tiles at a time, all n-tiles of a group column by column."""
+    out = set()
+    for pid in range(tiles_m * tiles_n - tail, tiles_m * tiles_n):
+        g, i = divmod(pid, group_m * tiles_n)
+        gm = min(tiles_m - g * group_m, group_m)
+        out.add(g * group_m + i % gm)
+    return sorted(out)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_dense_tail(dev, seed):
+    # shapes whose 256x256 tiles leave 1..48 past whole rounds, with a K that
+    # makes the tail launch worth it; every 64-row band of the m-tiles the
+    # tail touches is checked on 16 rows, the other m-tiles on one row each
+    rng = np.random.default_rng(7500 + seed)
+    for _ in range(100):
+        tn = int(rng.integers(4, 17))
+        tm = -(-(256 * int(rng.integers(1, 3)) + int(rng.integers(1, 49))) // tn)
+        M = 256 * tm - int(rng.integers(0, 200))
+        N = 256 * tn - 128 * int(rng.integers(0, 2))
+        K = 128 * int(rng.integers(12, 17))
+        mode = int(rng.integers(0, 2))
+        bm, bn, _, tail = fb.fp8_gemm_blockscaled_tile(M, N, K, mode)
+        if tail:
+            break
+    assert tail and (bm, bn) == (256, 256), "no shape with a tail drawn"
+    A, B = _codes(rng, (M, K)), _codes(rng, (N, K))
+    sA = _scales(rng, (K // 128, M))
+    sB = _scales(rng, (N // 128, K // 128) if mode == MODE_BLOCK else (K // 128, N))
+    C = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=dev)
+    fb.fp8_gemm_blockscaled(torch.from_numpy(A).to(dev), torch.from_numpy(sA).to(dev), torch.from_numpy(B).to(dev),
+                            torch.from_numpy(sB).to(dev), mode, out=C)
+    rows = {256 * t + int(rng.integers(0, 256)) for t in range(tm)}
+    for t in _tail_m_tiles(tm, -(-N // 256), tail):
+        for band in range(4):
+            rows |= {256 * t + 64 * band + int(r) for r in rng.integers(0, 64, 16)}
+    rows = np.array(sorted(r for r in rows if r < M))
+    ref, absref = oracle.gemm_ref_rows(A[rows], sA[:, rows], B, sB, mode)
+    torch.cuda.synchronize()
+    _check(C[rows], ref, absref, f"seed {seed}: gemm {M}x{N}x{K} mode {mode}, tail {tail}")
 
 
 def _expert_counts(rng):
