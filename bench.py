@@ -259,6 +259,12 @@ def _cast_ceilings(torch, dev, inputs):
     return out
 
 
+def _kernel_choice(fb, M, N, K, mode):
+    """The kernel fp8_gemm_blockscaled picks for an M x N x K problem."""
+    bm, bn, depth, tail = fb.fp8_gemm_blockscaled_tile(M, N, K, mode)
+    return {"tile": [bm, bn], "ring_depth": depth, "tail_tiles": tail}
+
+
 def setup_dense_fprop(torch, fb, dev, M=4096, N=7168, K=7168, fused=False, pow2=False):
     """Quantize X 1x128 and W 128x128, then the GEMM. With fused=True the GEMM
     writes the 1x128 quantization of its result (the next layer's FP8 input)
@@ -328,6 +334,7 @@ def setup_dense_fprop(torch, fb, dev, M=4096, N=7168, K=7168, fused=False, pow2=
            }[int(fused)]
     info = {
         "names": ["quant_act_1x128", "quant_w_128x128", gemm],
+        "kernel_choice": {} if fused or pow2 else {gemm: _kernel_choice(fb, M, N, K, fb.SCALE_BLOCK128)},
         "step_flops": flops,
         "work": {
             "quant_act_1x128": ("GB/s", M * K * 2 + M * K + M * K // 128 * 4),
@@ -371,6 +378,7 @@ def setup_tiny_fprop(torch, fb, dev, M=256, N=512, K=1024):
     flops = 2.0 * M * N * K
     info = {
         "names": ["quant_act_1x128", "quant_w_128x128", "gemm_blockscaled"],
+        "kernel_choice": {"gemm_blockscaled": _kernel_choice(fb, M, N, K, fb.SCALE_BLOCK128)},
         "step_flops": flops,
         "work": {"quant_act_1x128": ("GB/s", M * K * 4 + M * K + M * K // 128 * 4),
                  "quant_w_128x128": ("GB/s", N * K * 4 + N * K + N * K // 16384 * 4),
@@ -444,6 +452,8 @@ def setup_backward(torch, fb, dev, M=4096, N=7168, K=7168):
     qb = M * N * 2 + M * N + M * N // 128 * 4
     info = {
         "names": ["quant_act_1x128(dY)", "quant_act_128x1_T(dY)", "quant_act_128x1_T(X)", "gemm_dgrad", "gemm_wgrad"],
+        "kernel_choice": {"gemm_dgrad": _kernel_choice(fb, M, K, N, fb.SCALE_BLOCK128),
+                          "gemm_wgrad": _kernel_choice(fb, N, K, M, fb.SCALE_ROW)},
         "step_flops": 2 * flops,
         "work": {
             "quant_act_1x128(dY)": ("GB/s", qb),
@@ -872,6 +882,8 @@ def run_workload(torch, fb, dev, name, steps, warmup, ramp_ms, clock_ms=1500.0):
             # the same bytes through PyTorch's elementwise BF16 -> FP8 cast
             kernels[n]["cast_ceiling_us_median"] = round(ceiling_us[n], 2)
             kernels[n]["frac_of_cast_ceiling"] = round(ceiling_us[n] / percentile(ts, 0.5), 3)
+    for n, choice in info.pop("kernel_choice", {}).items():
+        kernels[n]["kernel"] = choice
     info.pop("ceilings", None)
     del step
     return info, ms_per_step, kernels, clk.summary(), ramp

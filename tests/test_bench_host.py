@@ -98,3 +98,11 @@ def test_source_digest_ignores_comments_only():
     assert bench._code_only(code) == bench._code_only(code.replace("one more", "plus one").replace("block", "b"))
     assert bench._code_only(code) != bench._code_only(code.replace("x + 1", "x + 2"))
     assert bench._code_only("a  =\n b;") == "a = b;"
+
+
+def test_kernel_choice_reports_the_library_pick():
+    import fp8_block_scaled_x1_amd as fb
+    assert bench._kernel_choice(fb, 4096, 7168, 7168, fb.SCALE_BLOCK128) == \
+        {"tile": [256, 224], "ring_depth": 3, "tail_tiles": 0}
+    assert bench._kernel_choice(fb, 7168, 7168, 4096, fb.SCALE_ROW) == \
+        {"tile": [256, 256], "ring_depth": 2, "tail_tiles": 16}
