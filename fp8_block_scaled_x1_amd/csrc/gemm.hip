@@ -19,7 +19,7 @@
 // 64x64 tiles and the hardware-scaled variant's 256x256 tiles):
 //   * one pipeline stage = one K chunk: A[BM][128] + B[BN][128] bytes plus the
 //     chunk's scale vectors, moved L2 -> LDS with direct-to-LDS loads (no VGPR
-//     staging); two or three stages per operand; one barrier per chunk;
+//     staging); two to four stages per operand; one barrier per chunk;
 //   * every direct-to-LDS load instruction reads 8 whole 128-byte rows (full
 //     cache lines); inside LDS the 16-byte column of row r is XOR-swizzled with
 //     (r & 7) ^ ((r >> 3) & 1), which keeps the MFMA fragment reads free of
@@ -84,7 +84,8 @@ struct Cfg {
   static constexpr bool kHoldB = NS <= MS;                    // hold the smaller operand
   static_assert(WGM * WGN == 8 || WGM * WGN == 4, "8 or 4 waves");
   static_assert(WM % 16 == 0 && WN % 16 == 0 && BM % 8 == 0 && BN % 8 == 0, "tile shape");
-  static_assert(DA >= 2 && DA <= 3 && DB >= 2 && DB <= 3, "rings two or three deep");
+  static_assert((DA >= 2 && DA <= 3 && DB >= 2 && DB <= 3) || (DA == 4 && DB == 4),
+                "rings two or three deep, or both four deep");
   static_assert(kAPieces <= 4 && kBPieces <= 4, "scale loads");
   static_assert(kLdsBytes <= 160 * 1024, "LDS");
 };
@@ -101,11 +102,13 @@ using Cfg224x256 = Cfg<224, 256, 2, 4, 2, 3>;
 using Cfg128x256 = Cfg<128, 256, 2, 4, 2, 2>;
 using Cfg128x128 = Cfg<128, 128, 4, 2, 2, 2>;
 using Cfg64x64 = Cfg<64, 64, 2, 2, 2, 2>;
-// The same two with both rings three deep: loads run two chunks ahead, which
+// The same two with deeper rings: loads run two or three chunks ahead, which
 // a lone workgroup on its CU needs to cover the load latency, at the price of
-// co-residency (128x128: one workgroup per CU; 64x64: three)
-using Cfg128x128d3 = Cfg<128, 128, 4, 2, 3, 3>;
+// co-residency (128x128 four deep: one workgroup per CU; 64x64 three deep:
+// three; 64x64 four deep: two)
+using Cfg128x128d4 = Cfg<128, 128, 4, 2, 4, 4>;
 using Cfg64x64d3 = Cfg<64, 64, 2, 2, 3, 3>;
+using Cfg64x64d4 = Cfg<64, 64, 2, 2, 4, 4>;
 // Subtiles of the tail launches (a last partial round of 256x256 tiles, dense
 // or grouped, recomputed over every CU), and how many of their workgroups
 // share a CU (LDS and registers)
@@ -221,7 +224,8 @@ __device__ __forceinline__ void wait_and_barrier() {
 template <class G, int ROW_MODE, int QOUT = 0, int HW = 0>
 __device__ __forceinline__ void run_tile(const Tile& t, uint8_t* smem) {
   constexpr int MS = G::MS, NS = G::NS, WM = G::WM, WN = G::WN;
-  constexpr bool kDeepA = G::DA == 3, kDeepB = G::DB == 3, kDeep = kDeepA || kDeepB;
+  constexpr bool kDeepA = G::DA >= 3, kDeepB = G::DB >= 3, kDeep = kDeepA || kDeepB;
+  constexpr int kAhead = G::DA == 4 ? 3 : 2;   // chunks a deep ring loads ahead
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -411,7 +415,9 @@ __device__ __forceinline__ void run_tile(const Tile& t, uint8_t* smem) {
   // are three deep). Only the deep loads, issued last, may still be in flight
   // at the next barrier. Chunk indices past the end are clamped: those loads
   // land in free slots and go unused.
-  constexpr int kND = (kDeepA ? kNA : 0) + (kDeepB ? kNB : 0);   // deep loads per chunk
+  // deep loads that may be in flight at a barrier: those of the kAhead - 1
+  // chunks after the one it waits for
+  constexpr int kND = ((kDeepA ? kNA : 0) + (kDeepB ? kNB : 0)) * (kAhead - 1);
   constexpr int kItems = kNA + kNB;
   constexpr int kSpread = kDeep ? NT : (NT + 1) / 2;
   auto barrier = [&](int x) {
@@ -424,8 +430,9 @@ __device__ __forceinline__ void run_tile(const Tile& t, uint8_t* smem) {
   auto refill_load = [&](int k, int kb) {
     const int k1 = min(kb + 1, nkb - 1), k2 = min(kb + 2, nkb - 1);
     if constexpr (kDeepA && kDeepB) {
-      if (k < kNA) a_load(k, k2, (kb + 2) % G::DA);
-      else b_load(k - kNA, k2, (kb + 2) % G::DB);
+      const int kd = min(kb + kAhead, nkb - 1);
+      if (k < kNA) a_load(k, kd, (kb + kAhead) % G::DA);
+      else b_load(k - kNA, kd, (kb + kAhead) % G::DB);
     } else if constexpr (kDeepA) {
       if (k < kNB) b_load(k, k1, (kb + 1) % G::DB);
       else a_load(k - kNB, k2, (kb + 2) % G::DA);
@@ -443,11 +450,14 @@ __device__ __forceinline__ void run_tile(const Tile& t, uint8_t* smem) {
       if (k * kSpread / kItems == t) refill_load(k, kb);
   };
 
-  // prologue: chunk 0 of both operands, chunk 1 of a three-deep operand
+  // prologue: chunk 0 of both operands, chunks 1 .. kAhead - 1 of a deep one
   issue_a(0, 0);
   issue_b(0, 0);
-  if constexpr (kDeepA) issue_a(min(1, nkb - 1), 1);
-  if constexpr (kDeepB) issue_b(min(1, nkb - 1), 1);
+#pragma unroll
+  for (int c = 1; c < kAhead; ++c) {
+    if constexpr (kDeepA) issue_a(min(c, nkb - 1), c);
+    if constexpr (kDeepB) issue_b(min(c, nkb - 1), c);
+  }
   barrier(0);
   // Retire every scalar load issued so far (kernel arguments), as the
   // compiler sees it: with one pending, each LDS wait in the loop would have
@@ -1018,12 +1028,12 @@ struct TileEst {
   double lat, thr;
 };
 enum DenseTile {
-  kT256x256, kT256x224, kT224x256, kT128x256, kT128x128, kT64x64, kT128x128d3, kT64x64d3, kDenseTiles
+  kT256x256, kT256x224, kT224x256, kT128x256, kT128x128, kT64x64, kT128x128d4, kT64x64d3, kT64x64d4, kDenseTiles
 };
 constexpr TileEst kTileEst[kDenseTiles] = {
     {256, 256, 2, 1, 80.0, 650.0}, {256, 224, 3, 1, 70.0, 637.0}, {224, 256, 3, 1, 70.0, 637.0},
     {128, 256, 2, 1, 54.0, 536.0}, {128, 128, 2, 2, 43.0, 531.0}, {64, 64, 2, 4, 33.0, 333.0},
-    {128, 128, 3, 1, 32.0, 499.0}, {64, 64, 3, 3, 23.0, 322.0}};
+    {128, 128, 4, 1, 30.0, 512.0}, {64, 64, 3, 3, 23.0, 322.0},    {64, 64, 4, 2, 22.0, 330.0}};
 template <class G>
 constexpr bool est_matches(DenseTile t) {
   return kTileEst[t].bm == G::BM && kTileEst[t].bn == G::BN && kTileEst[t].depth == (G::DA > G::DB ? G::DA : G::DB);
@@ -1031,7 +1041,8 @@ constexpr bool est_matches(DenseTile t) {
 static_assert(est_matches<Cfg256x256>(kT256x256) && est_matches<Cfg256x224>(kT256x224) &&
                   est_matches<Cfg224x256>(kT224x256) && est_matches<Cfg128x256>(kT128x256) &&
                   est_matches<Cfg128x128>(kT128x128) && est_matches<Cfg64x64>(kT64x64) &&
-                  est_matches<Cfg128x128d3>(kT128x128d3) && est_matches<Cfg64x64d3>(kT64x64d3),
+                  est_matches<Cfg128x128d4>(kT128x128d4) && est_matches<Cfg64x64d3>(kT64x64d3) &&
+                  est_matches<Cfg64x64d4>(kT64x64d4),
               "the estimate table follows the tile configurations");
 
 static_assert(est_matches<TailCfg>(kT64x64d3), "the tail subtiles are the three-deep 64x64 kernel");
@@ -1056,6 +1067,9 @@ DensePick pick_dense(int64_t M, int64_t N, int64_t K, hipStream_t stream) {
   int best = 0;
   double best_t = 0.0;
   for (int i = 0; i < kDenseTiles; ++i) {
+    // the three-deep 64x64 kernel only computes tails (for a whole problem the
+    // four-deep 128x128 kernel beats it wherever it holds three tiles per CU)
+    if (i == kT64x64d3) continue;
     const TileEst& c = kTileEst[i];
     const double t = tile_estimate(c, ((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn), cus, k);
     if (i == 0 || t < best_t) {
@@ -1362,9 +1376,9 @@ hipError_t launch_gemm_blockscaled(const uint8_t* A, const float* sA, const uint
     case kT128x256: return launch_dense<Cfg128x256, 0>(A, sA, B, sB, row_mode, C, nullptr, nullptr, M, N, K, stream);
     case kT128x128: return launch_dense<Cfg128x128, 0>(A, sA, B, sB, row_mode, C, nullptr, nullptr, M, N, K, stream);
     case kT64x64: return launch_dense<Cfg64x64, 0>(A, sA, B, sB, row_mode, C, nullptr, nullptr, M, N, K, stream);
-    case kT128x128d3:
-      return launch_dense<Cfg128x128d3, 0>(A, sA, B, sB, row_mode, C, nullptr, nullptr, M, N, K, stream);
-    case kT64x64d3: return launch_dense<Cfg64x64d3, 0>(A, sA, B, sB, row_mode, C, nullptr, nullptr, M, N, K, stream);
+    case kT128x128d4:
+      return launch_dense<Cfg128x128d4, 0>(A, sA, B, sB, row_mode, C, nullptr, nullptr, M, N, K, stream);
+    case kT64x64d4: return launch_dense<Cfg64x64d4, 0>(A, sA, B, sB, row_mode, C, nullptr, nullptr, M, N, K, stream);
     default: return launch_dense<Cfg256x256, 0>(A, sA, B, sB, row_mode, C, nullptr, nullptr, M, N, K, stream);
   }
 }

@@ -244,14 +244,14 @@ def test_tile_query_follows_the_shape(L):
 
     # a few tokens: 112 tiles of 256 rows would idle 144 CUs; one small tile
     # per CU, alone there, with its loads two chunks ahead
-    assert tile(64, 7168, 7168) == (64, 64, 3, 0)
-    assert tile(512, 7168, 7168) == (128, 128, 3, 0)
+    assert tile(64, 7168, 7168) == (64, 64, 4, 0)
+    assert tile(512, 7168, 7168) == (128, 128, 4, 0)
     assert tile(1024, 7168, 7168) == (128, 256, 2, 0)
     assert tile(4096, 2048, 7168) == (128, 256, 2, 0)
     assert tile(4096, 7168, 7168) == (256, 224, 3, 0)     # 512 tiles: two full rounds
     assert tile(4096, 4096, 4096) == (256, 256, 2, 0)
     assert tile(7168, 4096, 4096) == (224, 256, 3, 0)
-    assert tile(1, 128, 128) == (64, 64, 3, 0)
+    assert tile(1, 128, 128) == (64, 64, 4, 0)
     # 784 tiles of 256x256: three rounds, and the 16 left as 256 subtiles of 64x64
     assert tile(7168, 7168, 4096) == (256, 256, 2, 16)
     assert tile(5120, 7168, 7168) == (256, 256, 2, 48)

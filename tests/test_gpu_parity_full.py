@@ -64,10 +64,11 @@ TILE_CASES = [((4096, 4096, 256), (256, 256, 2, 0)),
               ((7168, 4096, 128), (224, 256, 3, 0)),
               ((777, 5120, 128), (128, 256, 2, 0)),      # ragged last m-tile (9 rows)
               ((3700, 2176, 128), (128, 128, 2, 0)),     # ragged last m-tile (116 rows)
-              ((1700, 2048, 128), (128, 128, 3, 0)),     # ragged last m-tile (36 rows)
+              ((1700, 2048, 128), (128, 128, 4, 0)),     # ragged last m-tile (36 rows)
               ((1300, 3072, 128), (64, 64, 2, 0)),       # ragged last m-tile (20 rows)
-              ((300, 640, 256), (64, 64, 3, 0)),         # ragged last m-tile (44 rows)
-              ((1, 128, 128), (64, 64, 3, 0))]           # one row
+              ((300, 640, 256), (64, 64, 4, 0)),         # ragged last m-tile (44 rows)
+              ((1, 128, 128), (64, 64, 4, 0))]           # one row
+# (the three-deep 64x64 kernel computes the tails: test_gemm_tail_launch)
 
 
 def test_tile_cases_cover_every_tile(dev):
