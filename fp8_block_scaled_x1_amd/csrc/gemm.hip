@@ -712,14 +712,20 @@ __device__ __forceinline__ void run_tile(const Tile& t, uint8_t* smem) {
     // The codes go through LDS like the BF16 epilogue: a row-major copy of
     // the tile's codes (and, for QOUT == 2, a column-major one), after the
     // row maxima; rows of BN (BM) bytes with their 16-byte pieces XOR-swizzled
-    // by the row's low four bits, which keeps both the 4-byte writes and the
-    // 16-byte reads free of bank conflicts.
+    // by the row's low bits (four for rows of 256 bytes, which keeps both the
+    // 4-byte writes and the 16-byte reads free of bank conflicts).
     constexpr int kRedBytes = (G::kWaves * WM * 4 + 15) / 16 * 16;
     constexpr int kQOff = kRedBytes, kQTOff = kQOff + G::BM * G::BN;
     static_assert(kQTOff + (QOUT == 2 ? G::BN * G::BM : 0) <= G::kLdsBytes, "code tiles fit the operand slots");
-    static_assert(G::BN == 256 && (QOUT == 1 || G::BM == 256), "code tile rows of 16 pieces");
-    // byte offset of (row, col) in a code tile with rows of 256 bytes
-    auto swz_off = [](int row, int col) { return row * 256 + ((((col >> 4) ^ row) & 15) << 4) + (col & 15); };
+    static_assert((G::BN == 256 || G::BN == 128) && (QOUT == 1 || (G::BM == 256 && G::BN == 256)),
+                  "code tile rows of 8 or 16 pieces");
+    // byte offset of (row, col) in a code tile with rows of ROWB bytes
+    auto swz_off_in = [](auto rowb, int row, int col) {
+      constexpr int R = decltype(rowb)::value, P = R / 16;
+      return row * R + ((((col >> 4) ^ row) & (P - 1)) << 4) + (col & 15);
+    };
+    auto swz_off = [&](int row, int col) { return swz_off_in(std::integral_constant<int, G::BN>{}, row, col); };
+    auto swz_off_t = [&](int row, int col) { return swz_off_in(std::integral_constant<int, G::BM>{}, row, col); };
     if constexpr (kGW == 1) wait_and_barrier<0>();   // every wave is done with the operand slots
     const int grp = (t.n0 + wn * WN) / kGroup;
     const bool group_ok = t.n0 + wn * WN < t.N;   // N % 128 == 0: a group is wholly in or out
@@ -774,7 +780,7 @@ __device__ __forceinline__ void run_tile(const Tile& t, uint8_t* smem) {
             const uint32_t sh = 8u * (uint32_t)q;
             const uint32_t out = ((w0 >> sh) & 0xFFu) | (((w1 >> sh) & 0xFFu) << 8) |
                                  (((w2 >> sh) & 0xFFu) << 16) | (((w3 >> sh) & 0xFFu) << 24);
-            *reinterpret_cast<uint32_t*>(smem + kQTOff + swz_off(n_col - t.n0, wm * WM + 16 * i + (lane & 12))) =
+            *reinterpret_cast<uint32_t*>(smem + kQTOff + swz_off_t(n_col - t.n0, wm * WM + 16 * i + (lane & 12))) =
                 out;
           }
         }
@@ -800,7 +806,7 @@ __device__ __forceinline__ void run_tile(const Tile& t, uint8_t* smem) {
         const int n = t.n0 + col, m = t.m0 + 16 * piece;
         if (n < t.N && m < t.row_end)
           *reinterpret_cast<uint4*>(t.QT + (int64_t)n * t.row_end + m) =
-              *reinterpret_cast<const uint4*>(smem + kQTOff + swz_off(col, 16 * piece));
+              *reinterpret_cast<const uint4*>(smem + kQTOff + swz_off_t(col, 16 * piece));
       }
     }
   }
@@ -989,13 +995,6 @@ __global__ __launch_bounds__(G::kThreads, 1) void grouped_wgrad_kernel(
   t.m0 = tm * G::BM; t.row_end = N;
   t.n0 = tn * G::BN; t.N = K; t.K = groups * BK; t.ld = ld;
   run_tile<G, 1>(t, smem);
-}
-
-// Estimated cost of a tile shape: full rounds of tiles over the CUs times the
-// tile area (per-tile time is proportional to its area).
-template <class G>
-int64_t round_cost(int64_t tiles, int cus) {
-  return ((tiles + cus - 1) / cus) * (int64_t)G::BM * G::BN;
 }
 
 // Compute units of the device the work runs on (the stream's device; the
@@ -1408,13 +1407,29 @@ hipError_t launch_gemm_blockscaled_q1x128(const uint8_t* A, const float* sA, con
                                           const float* sB, int row_mode, uint8_t* Q, float* sQ,
                                           int64_t M, int64_t N, int64_t K, hipStream_t stream) {
   using namespace gemm;
-  // tiles whose columns hold whole 128-column groups: 256x256 or 224x256
+  // tiles whose columns hold whole 128-column groups, by the dense GEMM's
+  // time estimate: 256x256, 224x256, and for problems with few tiles
+  // 128x256 or 128x128 (four deep)
   const int cus = device_cus(stream);
-  const int64_t tn = (N + 255) / 256;
-  const int64_t c0 = round_cost<Cfg256x256>(((M + 255) / 256) * tn, cus);
-  const int64_t c2 = round_cost<Cfg224x256>(((M + 223) / 224) * tn, cus);
-  if (c2 < c0) return launch_dense<Cfg224x256, 1>(A, sA, B, sB, row_mode, nullptr, Q, sQ, M, N, K, stream);
-  return launch_dense<Cfg256x256, 1>(A, sA, B, sB, row_mode, nullptr, Q, sQ, M, N, K, stream);
+  const double k = (double)K / 7168.0;
+  const DenseTile cand[] = {kT256x256, kT224x256, kT128x256, kT128x128d4};
+  DenseTile best = kT256x256;
+  double best_t = 0.0;
+  for (const DenseTile c : cand) {
+    const TileEst& e = kTileEst[c];
+    const double t = tile_estimate(e, ((M + e.bm - 1) / e.bm) * ((N + e.bn - 1) / e.bn), cus, k);
+    if (c == kT256x256 || t < best_t) {
+      best = c;
+      best_t = t;
+    }
+  }
+  switch (best) {
+    case kT224x256: return launch_dense<Cfg224x256, 1>(A, sA, B, sB, row_mode, nullptr, Q, sQ, M, N, K, stream);
+    case kT128x256: return launch_dense<Cfg128x256, 1>(A, sA, B, sB, row_mode, nullptr, Q, sQ, M, N, K, stream);
+    case kT128x128d4:
+      return launch_dense<Cfg128x128d4, 1>(A, sA, B, sB, row_mode, nullptr, Q, sQ, M, N, K, stream);
+    default: return launch_dense<Cfg256x256, 1>(A, sA, B, sB, row_mode, nullptr, Q, sQ, M, N, K, stream);
+  }
 }
 
 hipError_t launch_gemm_blockscaled_q1x128_q128x1T(const uint8_t* A, const float* sA, const uint8_t* B,

@@ -75,6 +75,26 @@ def test_fused_q1x128_random_codes(dev, M, N, K, mode):
     _fused_vs_oracle(dev, A, sA, B, sB, mode, f"fused {M}x{N}x{K} mode {mode}")
 
 
+# Shapes for which the fused entry point picks each of its tiles on a 256-CU
+# MI355X (the dense GEMM's time estimate over 256x256, 224x256, 128x256 and
+# 128x128 four deep; the shapes above all take 128x128): rows of every
+# 16-row band checked, both scale modes.
+FUSED_TILE_SHAPES = [(64, 2048, 1024),     # 128x128, four deep
+                     (1600, 2560, 512),    # 128x256 (last m-tile 64 rows)
+                     (4096, 4096, 256),    # 256x256
+                     (7168, 2048, 256)]    # 224x256
+
+
+@pytest.mark.parametrize("M,N,K", FUSED_TILE_SHAPES)
+@pytest.mark.parametrize("mode", [MODE_BLOCK, MODE_ROW])
+def test_fused_q1x128_every_tile(dev, M, N, K, mode):
+    A, B = _codes((M, K), 5 * M + N + K + mode), _codes((N, K), 31 + M + 7 * N + K)
+    sA = _scales((K // 128, M), 11 + M)
+    sB = _scales(_sb_shape(mode, N, K), 19 + N)
+    rows = sorted({min(16 * b + (5 * b) % 16, M - 1) for b in range(-(-M // 16))})
+    _fused_vs_oracle(dev, A, sA, B, sB, mode, f"fused {M}x{N}x{K} mode {mode}", rows=rows)
+
+
 def test_fused_q1x128_zero_groups(dev):
     # zero rows of A and a zero 128-column block of B give all-zero groups of
     # C: codes +0 and scale 1.0; a single nonzero column gives a group whose
