@@ -1397,10 +1397,30 @@ hipError_t launch_gemm_blockscaled_pow2(const uint8_t* A, const float* sA, const
                                         const float* sB, int row_mode, uint16_t* C, int64_t M,
                                         int64_t N, int64_t K, hipStream_t stream) {
   using namespace gemm;
-  // 4 waves of 128x128 with the accumulators in AGPRs: 11% faster than the
-  // 8-wave tiles at 4096x7168x7168, on a par or better on the other shapes
-  // measured
-  return launch_dense<Cfg256x256w4, 0, 1>(A, sA, B, sB, row_mode, C, nullptr, nullptr, M, N, K, stream);
+  // Large problems: 4 waves of 128x128 with the accumulators in AGPRs, 11%
+  // faster than the 8-wave tiles at 4096x7168x7168, on a par or better on
+  // the other shapes measured. Problems with few tiles: the four-deep
+  // 128x128 or 64x64 kernels, by the dense GEMM's time estimate (the large
+  // tile counted as a 256x256 one).
+  const int cus = device_cus(stream);
+  const double k = (double)K / 7168.0;
+  const DenseTile cand[] = {kT256x256, kT128x128d4, kT64x64d4};
+  DenseTile best = kT256x256;
+  double best_t = 0.0;
+  for (const DenseTile c : cand) {
+    const TileEst& e = kTileEst[c];
+    const double t = tile_estimate(e, ((M + e.bm - 1) / e.bm) * ((N + e.bn - 1) / e.bn), cus, k);
+    if (c == kT256x256 || t < best_t) {
+      best = c;
+      best_t = t;
+    }
+  }
+  switch (best) {
+    case kT128x128d4:
+      return launch_dense<Cfg128x128d4, 0, 1>(A, sA, B, sB, row_mode, C, nullptr, nullptr, M, N, K, stream);
+    case kT64x64d4: return launch_dense<Cfg64x64d4, 0, 1>(A, sA, B, sB, row_mode, C, nullptr, nullptr, M, N, K, stream);
+    default: return launch_dense<Cfg256x256w4, 0, 1>(A, sA, B, sB, row_mode, C, nullptr, nullptr, M, N, K, stream);
+  }
 }
 
 hipError_t launch_gemm_blockscaled_q1x128(const uint8_t* A, const float* sA, const uint8_t* B,

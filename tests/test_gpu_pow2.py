@@ -105,6 +105,24 @@ def test_pow2_gemm_random_codes(dev, M, N, K, mode):
     _check(C, ref, absref, f"pow2 gemm {M}x{N}x{K} mode {mode}")
 
 
+# shapes for which the power-of-two GEMM picks each of its kernels on a
+# 256-CU MI355X (its time estimate over 256x256 four-wave tiles and the
+# four-deep 128x128 and 64x64 ones); rows of every 16-row band checked
+@pytest.mark.parametrize("M,N,K", [(1000, 2048, 512),     # 64x64, four deep (ragged last m-tile)
+                                   (2000, 2048, 512),     # 128x128, four deep (ragged last m-tile)
+                                   (4096, 4096, 256)])    # 256x256, four waves
+@pytest.mark.parametrize("mode", [MODE_BLOCK, MODE_ROW])
+def test_pow2_gemm_every_tile(dev, M, N, K, mode):
+    A, B = _codes((M, K), 7 * M + N + K + mode), _codes((N, K), M + 11 * N + K)
+    sA = _pow2_scales((K // 128, M), M + 3)
+    sB = _pow2_scales((N // 128, K // 128) if mode == MODE_BLOCK else (K // 128, N), N + 4)
+    C = fb.fp8_gemm_blockscaled(A.to(dev), sA.to(dev), B.to(dev), sB.to(dev), mode, pow2=True)
+    rows = np.array(sorted({min(16 * b + (3 * b) % 16, M - 1) for b in range(-(-M // 16))}))
+    ref, absref = oracle.gemm_ref_rows(A.numpy(), sA.numpy(), B.numpy(), sB.numpy(), mode, rows=rows)
+    torch.cuda.synchronize()
+    _check(C[rows], ref, absref, f"pow2 gemm {M}x{N}x{K} mode {mode}")
+
+
 def test_pow2_gemm_extreme_scales(dev):
     # scales near both ends of the E8M0 range the quantizers produce
     M, N, K = 256, 256, 512
