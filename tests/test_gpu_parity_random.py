@@ -9,6 +9,8 @@ against the oracle, beyond the hand-picked cases of the other files.
 * Grouped GEMM: 1..16 experts whose row counts mix empty, small (<= 32),
   medium and past-one-pass (> 256) experts, so both the weight-streaming and
   the tile kernel run, alone and together; the whole output is checked.
+  Larger batches for the tile kernel with and without the tail launch of its
+  last partial round, checked on the experts holding the last tiles in full.
 * Quantizers: 1x128 (any M, F32 or BF16), 128x128 (with and without the
   transposed copy) and 128x1 transposed (any C) on values whose magnitude
   varies per column and per row, with outliers, bit for bit.
@@ -144,6 +146,55 @@ def test_random_grouped_gemm(dev, seed):
     ref, absref = oracle.grouped_gemm_ref(A, sA, B, sB, off)
     torch.cuda.synchronize()
     _check(C, ref, absref, f"seed {seed}: grouped counts {counts.tolist()} N={N} K={K}")
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_grouped_tile_and_tail(dev, seed):
+    # experts averaging more than 256 rows (the tile kernel) in batches whose
+    # 256x256 tiles leave 1..48 past whole rounds of 256 CUs (the tail launch
+    # takes those as 64x64 subtiles; 6 of the 8 seeds) or more (no tail):
+    # every row of the experts that hold the last tiles, every 16th elsewhere
+    rng = np.random.default_rng(8500 + seed)
+    want_tail = seed % 4 != 3
+    for _ in range(1000):
+        E = int(rng.integers(4, 25))
+        tn = int(rng.integers(1, 5))
+        mt = rng.integers(0, 9, E)
+        mt[rng.random(E) < 0.15] = 0
+        tiles = int(mt.sum()) * tn
+        rem = tiles % 256
+        if tiles > 256 and ((1 <= rem <= 48) if want_tail else rem > 48):
+            counts = np.where(mt > 0, 256 * (mt - 1) + rng.integers(1, 257, E), 0)
+            if counts.sum() > 256 * E:
+                break
+    else:
+        raise AssertionError("no batch drawn")
+    N, K = 256 * tn, 128 * int(rng.integers(1, 5))
+    off = np.zeros(E + 1, np.int32)
+    off[1:] = np.cumsum(counts)
+    M = int(off[-1])
+    A, B = _codes(rng, (M, K)), _codes(rng, (E, N, K))
+    sA, sB = _scales(rng, (K // 128, M)), _scales(rng, (E, N // 128, K // 128))
+    C = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=dev)
+    fb.fp8_grouped_gemm_blockscaled(torch.from_numpy(A).to(dev), torch.from_numpy(sA).to(dev),
+                                    torch.from_numpy(B).to(dev), torch.from_numpy(sB).to(dev),
+                                    torch.from_numpy(off).to(dev), out=C)
+    # the experts holding the last 48 tiles (tiles are numbered expert-major)
+    last, acc = set(), 0
+    for e in range(E - 1, -1, -1):
+        if acc >= 48:
+            break
+        if mt[e]:
+            last.add(e)
+            acc += int(mt[e]) * tn
+    rows = set(range(0, M, 16))
+    for e in last:
+        rows |= set(range(int(off[e]), int(off[e + 1])))
+    rows = np.array(sorted(rows))
+    ref, absref = oracle.grouped_gemm_ref(A, sA, B, sB, off, rows=rows)
+    torch.cuda.synchronize()
+    _check(C[rows], ref, absref, f"seed {seed}: grouped {E} experts, {tiles} tiles (past rounds: {tiles % 256}), "
+                                 f"N={N} K={K}")
 
 
 def _values(rng, shape, dtype):
