@@ -109,6 +109,9 @@ using Cfg64x64 = Cfg<64, 64, 2, 2, 2, 2>;
 using Cfg128x128d4 = Cfg<128, 128, 4, 2, 4, 4>;
 using Cfg64x64d3 = Cfg<64, 64, 2, 2, 3, 3>;
 using Cfg64x64d4 = Cfg<64, 64, 2, 2, 4, 4>;
+// For the two-layout quantizing epilogue on problems with few tiles: 128x128
+// with 8 waves of 128x16, so that each wave's rows are one 128x1 group
+using Cfg128x128q2 = Cfg<128, 128, 1, 8, 4, 4>;
 // Subtiles of the tail launches (a last partial round of 256x256 tiles, dense
 // or grouped, recomputed over every CU), and how many of their workgroups
 // share a CU (LDS and registers)
@@ -717,7 +720,7 @@ __device__ __forceinline__ void run_tile(const Tile& t, uint8_t* smem) {
     constexpr int kRedBytes = (G::kWaves * WM * 4 + 15) / 16 * 16;
     constexpr int kQOff = kRedBytes, kQTOff = kQOff + G::BM * G::BN;
     static_assert(kQTOff + (QOUT == 2 ? G::BN * G::BM : 0) <= G::kLdsBytes, "code tiles fit the operand slots");
-    static_assert((G::BN == 256 || G::BN == 128) && (QOUT == 1 || (G::BM == 256 && G::BN == 256)),
+    static_assert((G::BN == 256 || G::BN == 128) && (QOUT == 1 || G::BM == 256 || G::BM == 128),
                   "code tile rows of 8 or 16 pieces");
     // byte offset of (row, col) in a code tile with rows of ROWB bytes
     auto swz_off_in = [](auto rowb, int row, int col) {
@@ -1045,6 +1048,9 @@ static_assert(est_matches<Cfg256x256>(kT256x256) && est_matches<Cfg256x224>(kT25
               "the estimate table follows the tile configurations");
 
 static_assert(est_matches<TailCfg>(kT64x64d3), "the tail subtiles are the three-deep 64x64 kernel");
+// Cfg128x128q2 (measured with the two-layout epilogue)
+constexpr TileEst kQ2Small = {128, 128, 4, 1, 40.0, 380.0};
+static_assert(kQ2Small.bm == Cfg128x128q2::BM && kQ2Small.bn == Cfg128x128q2::BN, "estimate of Cfg128x128q2");
 
 // Estimated time (us) of `tiles` tiles of kernel c on `cus` CUs, K = k * 7168.
 double tile_estimate(const TileEst& c, int64_t tiles, int cus, double k) {
@@ -1457,7 +1463,16 @@ hipError_t launch_gemm_blockscaled_q1x128_q128x1T(const uint8_t* A, const float*
                                                   uint8_t* QT, float* sQT, int64_t M, int64_t N, int64_t K,
                                                   hipStream_t stream) {
   using namespace gemm;
-  // 256x256 tiles: each wave's 128 rows form one 128x1 group
+  // tiles whose waves hold 128 whole rows (one 128x1 group) and whose columns
+  // hold whole 128-column groups: 256x256, or for problems with few tiles
+  // 128x128 with 8 waves of 128x16, by the dense GEMM's time estimate
+  const int cus = device_cus(stream);
+  const double k = (double)K / 7168.0;
+  const TileEst& big = kTileEst[kT256x256];
+  const double t_big = tile_estimate(big, ((M + 255) / 256) * ((N + 255) / 256), cus, k);
+  const double t_small = tile_estimate(kQ2Small, ((M + 127) / 128) * ((N + 127) / 128), cus, k);
+  if (t_small < t_big)
+    return launch_dense<Cfg128x128q2, 2>(A, sA, B, sB, row_mode, nullptr, Q, sQ, M, N, K, stream, QT, sQT);
   return launch_dense<Cfg256x256, 2>(A, sA, B, sB, row_mode, nullptr, Q, sQ, M, N, K, stream, QT, sQT);
 }
 

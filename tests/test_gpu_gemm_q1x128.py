@@ -192,6 +192,8 @@ def _both_vs_oracle(dev, A, sA, B, sB, mode, what):
     assert_scales_equal(sQT.cpu().numpy(), sto, f"{what}: 128x1 scales")
 
 
+# these shapes take the 128x128 tiles of 8 waves of 128 rows; the full-size
+# layer below takes 256x256
 @pytest.mark.parametrize("M,N,K", [(128, 128, 128), (256, 256, 384), (384, 640, 256), (1024, 1280, 512),
                                    (640, 384, 1024)])
 @pytest.mark.parametrize("mode", [MODE_BLOCK, MODE_ROW])
