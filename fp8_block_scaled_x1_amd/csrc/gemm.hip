@@ -1142,7 +1142,7 @@ hipError_t launch_dense_tail(const uint8_t* A, const float* sA, const uint8_t* B
 // shared by the waves, one chunk ahead, with one barrier per chunk. Every load
 // is an ordinary vector load, so the compiler's own waits stay exact; the
 // barrier waits for LDS only and leaves the weight loads in flight. A pass
-// computes NSUB activation subtiles of 16 rows (its rows rounded up to 32),
+// computes NSUB activation subtiles of 16 rows (its rows rounded up to 16),
 // compiled once per NSUB so no subtile branches sit in the chunk loop. The
 // operands are swapped as in the tile kernel: lane l holds
 // C[m = 16i + l%16][n .. n+3].
@@ -1353,14 +1353,22 @@ __global__ __launch_bounds__(dec::kThreads, 1) void grouped_decode_kernel(
   for (int m0 = r0; m0 < r1; m0 += dec::kBM) {
     a.m0 = m0;
     a.rows = min(dec::kBM, r1 - m0);
-    switch ((a.rows + 31) / 32) {
-      case 1: dec::run_pass<2>(a, smem); break;
-      case 2: dec::run_pass<4>(a, smem); break;
-      case 3: dec::run_pass<6>(a, smem); break;
-      case 4: dec::run_pass<8>(a, smem); break;
-      case 5: dec::run_pass<10>(a, smem); break;
-      case 6: dec::run_pass<12>(a, smem); break;
-      case 7: dec::run_pass<14>(a, smem); break;
+    switch ((a.rows + 15) / 16) {
+      case 1: dec::run_pass<1>(a, smem); break;
+      case 2: dec::run_pass<2>(a, smem); break;
+      case 3: dec::run_pass<3>(a, smem); break;
+      case 4: dec::run_pass<4>(a, smem); break;
+      case 5: dec::run_pass<5>(a, smem); break;
+      case 6: dec::run_pass<6>(a, smem); break;
+      case 7: dec::run_pass<7>(a, smem); break;
+      case 8: dec::run_pass<8>(a, smem); break;
+      case 9: dec::run_pass<9>(a, smem); break;
+      case 10: dec::run_pass<10>(a, smem); break;
+      case 11: dec::run_pass<11>(a, smem); break;
+      case 12: dec::run_pass<12>(a, smem); break;
+      case 13: dec::run_pass<13>(a, smem); break;
+      case 14: dec::run_pass<14>(a, smem); break;
+      case 15: dec::run_pass<15>(a, smem); break;
       default: dec::run_pass<16>(a, smem); break;
     }
   }
