@@ -14,6 +14,7 @@ constexpr int64_t kG = 128;
 constexpr int64_t kI32 = (int64_t)1 << 31;
 
 bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+bool misaligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) != 0; }
 
 int status_of(hipError_t e) { return e == hipSuccess ? FP8BS_OK : FP8BS_ERR_LAUNCH; }
 
@@ -188,7 +189,8 @@ int fp8_grouped_gemm_blockscaled(const uint8_t* A, const float* sA, const uint8_
   if (E == 0 && M_total > 0) return FP8BS_ERR_SHAPE;   // rows with no expert
   if (M_total == 0 || N == 0) return FP8BS_OK;
   if (!A || !sA || !B || !sB || !C || !group_offsets) return FP8BS_ERR_NULL_PTR;
-  if (misaligned(A) || misaligned(sA) || misaligned(B) || misaligned(sB) || misaligned(C))
+  if (misaligned(A) || misaligned(sA) || misaligned(B) || misaligned(sB) || misaligned(C) ||
+      misaligned4(group_offsets))
     return FP8BS_ERR_ALIGN;
   return status_of(fp8bs::launch_grouped_gemm_blockscaled(A, sA, B, sB, C, group_offsets, E,
                                                           M_total, N, K, as_stream(stream)));
@@ -204,7 +206,7 @@ int fp8_quant_act_128x1_T_grouped(const void* x, int dtype, int64_t M_total, int
   if (M_total >= kI32 || C >= kI32 || ld / kG > 65535) return FP8BS_ERR_TOO_LARGE;
   if (M_total == 0 || C == 0) return FP8BS_OK;
   if (!x || !qT || !sT || !group_offsets) return FP8BS_ERR_NULL_PTR;
-  if (misaligned(x) || misaligned(qT) || misaligned(sT)) return FP8BS_ERR_ALIGN;
+  if (misaligned(x) || misaligned(qT) || misaligned(sT) || misaligned4(group_offsets)) return FP8BS_ERR_ALIGN;
   return status_of(fp8bs::launch_quant_act_128x1_T_grouped(x, dtype == FP8BS_BF16, M_total, C, group_offsets,
                                                            E, ld, qT, sT, as_stream(stream)));
 }
@@ -220,7 +222,8 @@ int fp8_grouped_gemm_wgrad(const uint8_t* A, const float* sA, const uint8_t* B, 
     return FP8BS_ERR_TOO_LARGE;
   if (E == 0 || N == 0 || K == 0) return FP8BS_OK;
   if (!A || !sA || !B || !sB || !C || !group_offsets) return FP8BS_ERR_NULL_PTR;
-  if (misaligned(A) || misaligned(sA) || misaligned(B) || misaligned(sB) || misaligned(C))
+  if (misaligned(A) || misaligned(sA) || misaligned(B) || misaligned(sB) || misaligned(C) ||
+      misaligned4(group_offsets))
     return FP8BS_ERR_ALIGN;
   return status_of(fp8bs::launch_grouped_gemm_wgrad(A, sA, B, sB, C, group_offsets, E, M_total, N, K, ld,
                                                     as_stream(stream)));
@@ -246,8 +249,8 @@ int dispatch_checks(const void* x, int dtype, int64_t T, int64_t K, const int32_
   if (P > 0 && (!topk_ids || !pos || !src_row)) return FP8BS_ERR_NULL_PTR;
   if (P > 0 && K > 0 && (!x || !q || !s)) return FP8BS_ERR_NULL_PTR;
   if (misaligned(x) || misaligned(q) || misaligned(s)) return FP8BS_ERR_ALIGN;
-  auto mis4 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) != 0; };
-  if (mis4(topk_ids) || mis4(offsets) || mis4(pos) || mis4(src_row)) return FP8BS_ERR_ALIGN;
+  if (misaligned4(topk_ids) || misaligned4(offsets) || misaligned4(pos) || misaligned4(src_row))
+    return FP8BS_ERR_ALIGN;
   return FP8BS_OK;
 }
 }  // namespace
@@ -268,18 +271,10 @@ int fp8_moe_dispatch_noalloc(const void* x, int dtype, int64_t T, int64_t K, con
 int fp8_moe_dispatch(const void* x, int dtype, int64_t T, int64_t K, const int32_t* topk_ids, int topk, int E,
                      uint8_t* q, float* s, int32_t* offsets, int32_t* pos, int32_t* src_row, void* workspace,
                      void* stream) {
-  if (!valid_dtype(dtype)) return FP8BS_ERR_DTYPE;
-  if (T < 0 || K < 0 || K % kG || topk < 1 || topk > 64 || E < 1 || E > fp8bs::moe_max_experts())
-    return FP8BS_ERR_SHAPE;
-  const int64_t P = T * topk;
-  if (P >= kI32 || K >= kI32 || (K / kG + 3) / 4 > 65535 || (T + 7) / 8 >= (int64_t)1 << 27)
-    return FP8BS_ERR_TOO_LARGE;
-  if (!offsets) return FP8BS_ERR_NULL_PTR;
-  if (P > 0 && (!topk_ids || !pos || !src_row || !workspace)) return FP8BS_ERR_NULL_PTR;
-  if (P > 0 && K > 0 && (!x || !q || !s)) return FP8BS_ERR_NULL_PTR;
-  if (misaligned(x) || misaligned(q) || misaligned(s)) return FP8BS_ERR_ALIGN;
-  auto mis4 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) != 0; };
-  if (mis4(topk_ids) || mis4(offsets) || mis4(pos) || mis4(src_row) || mis4(workspace)) return FP8BS_ERR_ALIGN;
+  const int st = dispatch_checks(x, dtype, T, K, topk_ids, topk, E, q, s, offsets, pos, src_row);
+  if (st != FP8BS_OK) return st;
+  if (T * topk > 0 && !workspace) return FP8BS_ERR_NULL_PTR;
+  if (misaligned4(workspace)) return FP8BS_ERR_ALIGN;
   return status_of(fp8bs::launch_moe_dispatch(x, dtype == FP8BS_BF16, T, K, topk_ids, topk, E, q, s, offsets,
                                               pos, src_row, static_cast<int32_t*>(workspace),
                                               as_stream(stream)));
@@ -292,7 +287,7 @@ int fp8_moe_combine(const uint16_t* Y, const int32_t* pos, const float* w, int64
   if (T == 0 || N == 0) return FP8BS_OK;
   if (!Y || !pos || !w || !out) return FP8BS_ERR_NULL_PTR;
   if (misaligned(Y) || misaligned(out)) return FP8BS_ERR_ALIGN;
-  if ((reinterpret_cast<uintptr_t>(pos) & 3u) || (reinterpret_cast<uintptr_t>(w) & 3u)) return FP8BS_ERR_ALIGN;
+  if (misaligned4(pos) || misaligned4(w)) return FP8BS_ERR_ALIGN;
   return status_of(fp8bs::launch_moe_combine(Y, pos, w, T, topk, N, out, as_stream(stream)));
 }
 

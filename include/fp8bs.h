@@ -222,9 +222,10 @@ FP8BS_API int fp8_gemm_blockscaled_q1x128_q128x1T(const uint8_t* A, const float*
  *   A   [M_total][K]         uint8     sA [K/128][M_total] float32
  *   B   [E][N][K]            uint8     sB [E][N/128][K/128] float32
  *   C   [M_total][N]         BF16 bits
- *   group_offsets  DEVICE int32[E+1], off[0] = 0, non-decreasing,
- *                  off[E] = M_total (precondition, not checked on the host;
- *                  the kernels clamp every row index into [0, M_total)).
+ *   group_offsets  DEVICE int32[E+1], 4-byte aligned, off[0] = 0,
+ *                  non-decreasing, off[E] = M_total (precondition, not checked
+ *                  on the host; the kernels clamp every row index into
+ *                  [0, M_total)).
  * K and N multiples of 128; E >= 0; M_total >= 0.
  */
 FP8BS_API int fp8_grouped_gemm_blockscaled(const uint8_t* A, const float* sA,
@@ -246,8 +247,9 @@ FP8BS_API int fp8_grouped_gemm_blockscaled(const uint8_t* A, const float* sA,
  *   x    [M_total][C]    F32 or BF16 (dtype), rows grouped by expert
  *   qT   [C][ld]         uint8 codes; columns 128 * P_E .. ld-1 are not written
  *   sT   [ld/128][C]     float32; rows P_E .. are not written
- *   group_offsets  DEVICE int32[E+1], off[0] = 0, non-decreasing,
- *                  off[E] = M_total (precondition as for the grouped GEMM)
+ *   group_offsets  DEVICE int32[E+1], 4-byte aligned, off[0] = 0,
+ *                  non-decreasing, off[E] = M_total (precondition as for the
+ *                  grouped GEMM)
  * C a multiple of 128; ld a multiple of 128 with ld >= M_total + 127 E (room
  * for every expert's padding); E >= 0, M_total >= 0 (M_total == 0: no-op).
  * FP8BS_ERR_TOO_LARGE if M_total >= 2^31 or ld / 128 > 65535.

@@ -110,6 +110,7 @@ def test_grouped_validation(L):
     assert f(P, P, P, P, P, NULL, 2, 4, 128, 128, NULL) == -1   # offsets missing
     assert f(P, P, P, P, P, P, 2, 4, 128, 100, NULL) == -2
     assert f(MIS, P, P, P, P, P, 2, 4, 128, 128, NULL) == -3
+    assert f(P, P, P, P, P, P + 2, 2, 4, 128, 128, NULL) == -3  # offsets not 4-byte aligned
     assert f(NULL, NULL, NULL, NULL, NULL, NULL, 3, 0, 128, 128, NULL) == 0
 
 
@@ -145,11 +146,13 @@ def test_grouped_backward_validation(L):
     assert q(P, 3, 300, 128, P, 2, ld, P, P, NULL) == -4
     assert q(P, 1, 300, 128, NULL, 2, ld, P, P, NULL) == -1
     assert q(MIS, 1, 300, 128, P, 2, ld, P, P, NULL) == -3
+    assert q(P, 1, 300, 128, P + 2, 2, ld, P, P, NULL) == -3       # offsets not 4-byte aligned
     assert q(NULL, 1, 0, 128, NULL, 2, fb.grouped_ld(0, 2), NULL, NULL, NULL) == 0   # no rows: no-op
     w = L.fp8_grouped_gemm_wgrad
     assert w(P, P, P, P, P, P, 2, 300, 128, 128, ld - 128, NULL) == -2
     assert w(P, P, P, P, P, P, 2, 300, 100, 128, ld, NULL) == -2
     assert w(P, P, P, P, NULL, P, 2, 300, 128, 128, ld, NULL) == -1
+    assert w(P, P, P, P, P, P + 2, 2, 300, 128, 128, ld, NULL) == -3  # offsets not 4-byte aligned
     assert w(P, P, P, P, P, P, 2, 300, 1 << 20, 128, 1 << 12, NULL) == -7
     assert w(NULL, NULL, NULL, NULL, NULL, NULL, 0, 0, 128, 128, 0, NULL) == 0
     assert fb.grouped_ld(300, 2) == 640 and fb.grouped_ld(0, 0) == 0
