@@ -507,13 +507,15 @@ __device__ __forceinline__ void run_tile(const Tile& t, uint8_t* smem) {
           promote_step(t - 1, p_prev, sc, fc, S);
         else if (kCarry)
           promote_step(NT - 1, p_prev, sc, f_prev, S);
-        // one MFMA, then a group of promotion FMAs, so the two pipes overlap
+        // one MFMA, then a group of six VALU instructions (the promotion),
+        // so the two pipes overlap (row mode, with two operations per
+        // element, measured 1-2% faster with six than with eight)
         if (promoting) {
 #pragma unroll
           for (int h = 0; h < NH; ++h) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             if (h == 0 && t + 1 < NT) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, ROW_MODE ? 8 : 6, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
           }
         }
 #pragma unroll
