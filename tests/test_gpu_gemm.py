@@ -150,6 +150,21 @@ def test_grouped_gemm_random(dev, counts, N, K):
     _check(C, ref, absref, f"grouped {counts} N={N} K={K}")
 
 
+def test_grouped_decode_every_subtile_count(dev):
+    # the weight-streaming kernel is compiled once per count of 16-row
+    # activation subtiles (1 .. 16): give it every count, with the rows
+    # filling the last subtile and with one row in it (mean <= 256 rows per
+    # expert, so every expert takes that kernel)
+    full = [16 * k for k in range(1, 17)]
+    ragged = [16 * k - 15 for k in range(1, 17)]
+    counts = [c for pair in zip(full, ragged[::-1]) for c in pair]
+    assert sum(counts) <= 256 * len(counts)
+    A, sA, B, sB, off, C = _grouped_case(dev, counts, 256, 256, 4242)
+    ref, absref = oracle.grouped_gemm_ref(A.numpy(), sA.numpy(), B.numpy(), sB.numpy(), off)
+    torch.cuda.synchronize()
+    _check(C, ref, absref, "decode kernel, every subtile count")
+
+
 def test_grouped_gemm_decode_workload(dev):
     d = workloads.decode_grouped(device=dev)
     off = d["offsets"]
