@@ -24,12 +24,27 @@
 namespace fp8bs {
 
 // ---------------------------------------------------------------------------
-// Loads of 8 consecutive high-precision elements as FP32 (exact widening).
+// 16-byte load with a non-temporal hint (the `nt` bit of the load). The
+// quantizers read every input byte exactly once; with the hint their BF16
+// passes ran 5-15% faster from HBM on the MI355X (128x1 over a 4096x7168
+// tensor 25.4 -> 21.7 us, 1x128 over 65536x7168 245 -> 227 us, 128x128 over
+// 7168x7168 29.9 -> 28.5 us), where without it the 128x1 pass's address unit
+// was stalled by the vector L1 seven times longer than the 1x128 pass's.
+// ---------------------------------------------------------------------------
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load16_stream(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// ---------------------------------------------------------------------------
+// Loads of 8 consecutive high-precision elements as FP32 (exact widening);
+// BF16 inputs through the streaming load above.
 // ---------------------------------------------------------------------------
 template <bool BF16>
 __device__ __forceinline__ void load8(const void* base, int64_t elem, float v[8]) {
   if constexpr (BF16) {
-    const uint4 d = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(base) + elem);
+    const uint4 d = load16_stream(reinterpret_cast<const uint16_t*>(base) + elem);
     const uint32_t w[4] = {d.x, d.y, d.z, d.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -388,7 +403,7 @@ __global__ __launch_bounds__(256) void quant_act_128x1_T_wave_kernel(
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int r = GROUPED ? min(tb + i, n_rows - 1) : tb + i;
-    raw[i] = *reinterpret_cast<const uint4*>(x + (row0 + r) * C + (cok ? ch : 0));
+    raw[i] = load16_stream(x + (row0 + r) * C + (cok ? ch : 0));
   }
   // token tb + i, channel ch + j, widened exactly to FP32 (rows past the
   // group's end read as zeros)
