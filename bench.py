@@ -422,9 +422,7 @@ def setup_backward(torch, fb, dev, M=4096, N=7168, K=7168):
             "dW": torch.empty((N, K), dtype=torch.bfloat16, device=dev),
         })
         del qw, sw
-    ceilings = _cast_ceilings(torch, dev, {"quant_act_1x128(dY)": sets[0]["dY"],
-                                           "quant_act_128x1_T(dY)": sets[0]["dY"],
-                                           "quant_act_128x1_T(X)": sets[0]["X"]})
+    ceilings = _cast_ceilings(torch, dev, {"quant_act_128x1_T(X)": sets[0]["X"]})
     L = fb.lib()
     stream = torch.cuda.current_stream(dev).cuda_stream
     state = {"i": 0}
@@ -433,9 +431,9 @@ def setup_backward(torch, fb, dev, M=4096, N=7168, K=7168):
         s = sets[state["i"] % R]
         state["i"] += 1
         timer.mark()
-        rc = L.fp8_quant_act_1x128(s["dY"].data_ptr(), fb.BF16, M, N, s["qdy"].data_ptr(), s["sdy"].data_ptr(), stream)
-        timer.mark()
-        rc |= L.fp8_quant_act_128x1_T(s["dY"].data_ptr(), fb.BF16, M, N, s["qdyT"].data_ptr(), s["sdyT"].data_ptr(), stream)
+        # dY both ways in one pass: 1x128 for Dgrad, 128x1 transposed for Wgrad
+        rc = L.fp8_quant_act_1x128_128x1_T(s["dY"].data_ptr(), fb.BF16, M, N, s["qdy"].data_ptr(), s["sdy"].data_ptr(),
+                                           s["qdyT"].data_ptr(), s["sdyT"].data_ptr(), stream)
         timer.mark()
         rc |= L.fp8_quant_act_128x1_T(s["X"].data_ptr(), fb.BF16, M, K, s["qxT"].data_ptr(), s["sxT"].data_ptr(), stream)
         timer.mark()
@@ -449,15 +447,13 @@ def setup_backward(torch, fb, dev, M=4096, N=7168, K=7168):
             raise RuntimeError(f"libfp8bs call failed ({rc})")
 
     flops = 2.0 * M * N * K
-    qb = M * N * 2 + M * N + M * N // 128 * 4
     info = {
-        "names": ["quant_act_1x128(dY)", "quant_act_128x1_T(dY)", "quant_act_128x1_T(X)", "gemm_dgrad", "gemm_wgrad"],
+        "names": ["quant_act_1x128_128x1_T(dY)", "quant_act_128x1_T(X)", "gemm_dgrad", "gemm_wgrad"],
         "kernel_choice": {"gemm_dgrad": _kernel_choice(fb, M, K, N, fb.SCALE_BLOCK128),
                           "gemm_wgrad": _kernel_choice(fb, N, K, M, fb.SCALE_ROW)},
         "step_flops": 2 * flops,
         "work": {
-            "quant_act_1x128(dY)": ("GB/s", qb),
-            "quant_act_128x1_T(dY)": ("GB/s", qb),
+            "quant_act_1x128_128x1_T(dY)": ("GB/s", M * N * 2 + 2 * (M * N + M * N // 128 * 4)),
             "quant_act_128x1_T(X)": ("GB/s", M * K * 2 + M * K + M * K // 128 * 4),
             "gemm_dgrad": ("TFLOP/s", flops),
             "gemm_wgrad": ("TFLOP/s", flops),
@@ -539,9 +535,9 @@ def setup_moe(torch, fb, dev):
 
 def setup_moe_backward(torch, fb, dev):
     """Backward of the grouped expert GEMMs, down then up: per projection the
-    1x128 quantizer of dY and the grouped Dgrad on the weights' transposed
-    copies, then the grouped 128x1 transposed quantizers of dY and of the
-    forward input, and the per-expert Wgrad."""
+    quantizer of dY into both layouts (1x128 and the experts' 128x1 groups),
+    the grouped Dgrad on the weights' transposed copies, the grouped 128x1
+    transposed quantizer of the forward input, and the per-expert Wgrad."""
     import workloads
     d = workloads.grouped_moe_backward(device=dev)
     off = torch.from_numpy(d["offsets"]).to(dev)
@@ -577,15 +573,15 @@ def setup_moe_backward(torch, fb, dev):
         timer.mark()
         for p in proj:
             N, K = p["N"], p["K"]
-            rc |= L.fp8_quant_act_1x128(p["dY"].data_ptr(), fb.BF16, Mt, N, p["qdy"].data_ptr(), p["sdy"].data_ptr(),
-                                        stream)
+            # dY both ways in one pass: 1x128 for the grouped Dgrad, the
+            # experts' 128x1 groups for the grouped Wgrad
+            rc |= L.fp8_quant_act_1x128_128x1_T_grouped(p["dY"].data_ptr(), fb.BF16, Mt, N, off.data_ptr(), E, ld,
+                                                        p["qdy"].data_ptr(), p["sdy"].data_ptr(),
+                                                        p["qdyT"].data_ptr(), p["sdyT"].data_ptr(), stream)
             timer.mark()
             rc |= L.fp8_grouped_gemm_blockscaled(p["qdy"].data_ptr(), p["sdy"].data_ptr(), p["qwT"].data_ptr(),
                                                  p["swT"].data_ptr(), p["dX"].data_ptr(), off.data_ptr(), E, Mt, K, N,
                                                  stream)
-            timer.mark()
-            rc |= L.fp8_quant_act_128x1_T_grouped(p["dY"].data_ptr(), fb.BF16, Mt, N, off.data_ptr(), E, ld,
-                                                  p["qdyT"].data_ptr(), p["sdyT"].data_ptr(), stream)
             timer.mark()
             rc |= L.fp8_quant_act_128x1_T_grouped(p["X"].data_ptr(), fb.BF16, Mt, K, off.data_ptr(), E, ld,
                                                   p["qxT"].data_ptr(), p["sxT"].data_ptr(), stream)
@@ -601,9 +597,8 @@ def setup_moe_backward(torch, fb, dev):
     for p in proj:
         N, K, t = p["N"], p["K"], p["tag"]
         f = 2.0 * Mt * N * K
-        for n, w in ((f"quant_act_1x128(dY_{t})", ("GB/s", Mt * N * 3 + Mt * N // 32)),
+        for n, w in ((f"quant_1x128_128x1_T_grouped(dY_{t})", ("GB/s", Mt * N * 4 + Mt * N // 16)),
                      (f"grouped_dgrad_{t}", ("TFLOP/s", f)),
-                     (f"quant_128x1_T_grouped(dY_{t})", ("GB/s", Mt * N * 3 + Mt * N // 32)),
                      (f"quant_128x1_T_grouped(X_{t})", ("GB/s", Mt * K * 3 + Mt * K // 32)),
                      (f"grouped_wgrad_{t}", ("TFLOP/s", f))):
             names.append(n)

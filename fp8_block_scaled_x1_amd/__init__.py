@@ -9,7 +9,8 @@ from ._lib import (ABI_VERSION, BF16, F32, LIB_PATH, SCALE_BLOCK128, SCALE_ROW, 
                    fp8_gemm_blockscaled, fp8_gemm_blockscaled_q1x128, fp8_gemm_blockscaled_tile, fp8_gemm_blockscaled_q1x128_q128x1T,
                    fp8_grouped_gemm_blockscaled,
                    fp8_grouped_gemm_wgrad, fp8_moe_combine, fp8_moe_dispatch, fp8_moe_dispatch_noalloc, fp8_quant_act_128x1_T,
-                   fp8_quant_act_128x1_T_grouped,
+                   fp8_quant_act_128x1_T_grouped, fp8_quant_act_1x128_128x1_T,
+                   fp8_quant_act_1x128_128x1_T_grouped,
                    fp8_quant_act_1x128, fp8_quant_w_128x128, grouped_ld, lib, status_string)
 
 __all__ = [
@@ -18,5 +19,7 @@ __all__ = [
     "fp8_grouped_gemm_blockscaled",
     "fp8_grouped_gemm_wgrad", "fp8_moe_combine", "fp8_moe_dispatch", "fp8_moe_dispatch_noalloc", "fp8_quant_act_128x1_T",
     "fp8_quant_act_128x1_T_grouped",
+    "fp8_quant_act_1x128_128x1_T",
+    "fp8_quant_act_1x128_128x1_T_grouped",
     "fp8_quant_act_1x128", "fp8_quant_w_128x128", "grouped_ld", "lib", "status_string",
 ]

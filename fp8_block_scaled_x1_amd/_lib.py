@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libfp8bs.so")
 
 F32, BF16 = 0, 1
 SCALE_BLOCK128, SCALE_ROW = 0, 1
-ABI_VERSION = 10
+ABI_VERSION = 11
 
 _c_int64 = ctypes.c_int64
 _vp = ctypes.c_void_p
@@ -42,6 +42,9 @@ _SIGNATURES = {
                                      _c_int64, _vp],
     "fp8_quant_act_128x1_T_grouped": [_vp, ctypes.c_int, _c_int64, _c_int64, _vp, ctypes.c_int, _c_int64, _vp,
                                       _vp, _vp],
+    "fp8_quant_act_1x128_128x1_T": [_vp, ctypes.c_int, _c_int64, _c_int64, _vp, _vp, _vp, _vp, _vp],
+    "fp8_quant_act_1x128_128x1_T_grouped": [_vp, ctypes.c_int, _c_int64, _c_int64, _vp, ctypes.c_int, _c_int64,
+                                            _vp, _vp, _vp, _vp, _vp],
     "fp8_grouped_gemm_wgrad": [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _c_int64, _c_int64, _c_int64,
                                _c_int64, _vp],
     "fp8_moe_dispatch": [_vp, ctypes.c_int, _c_int64, _c_int64, _vp, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp,
@@ -155,6 +158,24 @@ def fp8_quant_act_128x1_T(x, pow2=False):
     fn = "fp8_quant_act_128x1_T_pow2" if pow2 else "fp8_quant_act_128x1_T"
     _check(fn, getattr(lib(), fn)(px, _in_dtype(x), M, C, qT.data_ptr(), sT.data_ptr(), _stream(x)))
     return qT, sT
+
+
+def fp8_quant_act_1x128_128x1_T(x):
+    """x[M][C] -> (q [M][C], s [C/128][M], qT [C][M], sT [M/128][C]): the 1x128
+    and the transposed 128x1 quantization in one pass; M, C multiples of 128."""
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D")
+    M, C = x.shape
+    px = _dev(x, "x", (torch.float32, torch.bfloat16))
+    dev = x.device
+    q = torch.empty((M, C), dtype=torch.uint8, device=dev)
+    s = torch.empty((C // 128, M), dtype=torch.float32, device=dev)
+    qT = torch.empty((C, M), dtype=torch.uint8, device=dev)
+    sT = torch.empty((M // 128, C), dtype=torch.float32, device=dev)
+    _check("fp8_quant_act_1x128_128x1_T",
+           lib().fp8_quant_act_1x128_128x1_T(px, _in_dtype(x), M, C, q.data_ptr(), s.data_ptr(), qT.data_ptr(),
+                                             sT.data_ptr(), _stream(x)))
+    return q, s, qT, sT
 
 
 def _gemm_operands(A, sA, B, sB, b_scale_mode):
@@ -280,6 +301,30 @@ def fp8_quant_act_128x1_T_grouped(x, group_offsets, ld=None):
            lib().fp8_quant_act_128x1_T_grouped(px, _in_dtype(x), M, C, po, E, ld, qT.data_ptr(), sT.data_ptr(),
                                                _stream(x)))
     return qT, sT
+
+
+def fp8_quant_act_1x128_128x1_T_grouped(x, group_offsets, ld=None):
+    """x[M_total][C] rows grouped by expert -> (q [M_total][C], s [C/128][M_total],
+    qT [C][ld], sT [ld/128][C]): fp8_quant_act_1x128 and
+    fp8_quant_act_128x1_T_grouped in one pass."""
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D")
+    M, C = x.shape
+    E = group_offsets.shape[0] - 1
+    if E < 0:
+        raise ValueError("group_offsets must have E+1 entries")
+    ld = grouped_ld(M, E) if ld is None else int(ld)
+    px = _dev(x, "x", (torch.float32, torch.bfloat16))
+    po = _dev(group_offsets, "group_offsets", (torch.int32,))
+    dev = x.device
+    q = torch.empty((M, C), dtype=torch.uint8, device=dev)
+    s = torch.empty((C // 128, M), dtype=torch.float32, device=dev)
+    qT = torch.empty((C, ld), dtype=torch.uint8, device=dev)
+    sT = torch.empty((ld // 128, C), dtype=torch.float32, device=dev)
+    _check("fp8_quant_act_1x128_128x1_T_grouped",
+           lib().fp8_quant_act_1x128_128x1_T_grouped(px, _in_dtype(x), M, C, po, E, ld, q.data_ptr(), s.data_ptr(),
+                                                     qT.data_ptr(), sT.data_ptr(), _stream(x)))
+    return q, s, qT, sT
 
 
 def fp8_grouped_gemm_wgrad(A, sA, B, sB, group_offsets, M_total, out=None):

@@ -211,6 +211,38 @@ int fp8_quant_act_128x1_T_grouped(const void* x, int dtype, int64_t M_total, int
                                                            E, ld, qT, sT, as_stream(stream)));
 }
 
+int fp8_quant_act_1x128_128x1_T(const void* x, int dtype, int64_t M, int64_t C, uint8_t* q, float* s,
+                                uint8_t* qT, float* sT, void* stream) {
+  if (!valid_dtype(dtype)) return FP8BS_ERR_DTYPE;
+  if (M < 0 || C < 0 || M % kG || C % kG) return FP8BS_ERR_SHAPE;
+  if (M >= kI32 || C >= kI32 || M / kG > 65535 || (C / kG + 3) / 4 > 65535 || (M + 7) / 8 >= (int64_t)1 << 27)
+    return FP8BS_ERR_TOO_LARGE;
+  if (M == 0 || C == 0) return FP8BS_OK;
+  if (!x || !q || !s || !qT || !sT) return FP8BS_ERR_NULL_PTR;
+  if (misaligned(x) || misaligned(q) || misaligned(s) || misaligned(qT) || misaligned(sT)) return FP8BS_ERR_ALIGN;
+  return status_of(fp8bs::launch_quant_act_dual(x, dtype == FP8BS_BF16, M, C, q, s, qT, sT, nullptr, 0, M,
+                                                as_stream(stream)));
+}
+
+int fp8_quant_act_1x128_128x1_T_grouped(const void* x, int dtype, int64_t M_total, int64_t C,
+                                        const int32_t* group_offsets, int E, int64_t ld, uint8_t* q, float* s,
+                                        uint8_t* qT, float* sT, void* stream) {
+  if (!valid_dtype(dtype)) return FP8BS_ERR_DTYPE;
+  if (E < 0 || M_total < 0 || C < 0 || C % kG || ld < 0 || ld % kG) return FP8BS_ERR_SHAPE;
+  if (E == 0 && M_total > 0) return FP8BS_ERR_SHAPE;     // rows with no expert
+  if (ld < M_total + (kG - 1) * E) return FP8BS_ERR_SHAPE;
+  if (M_total >= kI32 || C >= kI32 || ld / kG > 65535 || (C / kG + 3) / 4 > 65535 ||
+      (M_total + 7) / 8 >= (int64_t)1 << 27)
+    return FP8BS_ERR_TOO_LARGE;
+  if (M_total == 0 || C == 0) return FP8BS_OK;
+  if (!x || !q || !s || !qT || !sT || !group_offsets) return FP8BS_ERR_NULL_PTR;
+  if (misaligned(x) || misaligned(q) || misaligned(s) || misaligned(qT) || misaligned(sT) ||
+      misaligned4(group_offsets))
+    return FP8BS_ERR_ALIGN;
+  return status_of(fp8bs::launch_quant_act_dual(x, dtype == FP8BS_BF16, M_total, C, q, s, qT, sT, group_offsets,
+                                                E, ld, as_stream(stream)));
+}
+
 int fp8_grouped_gemm_wgrad(const uint8_t* A, const float* sA, const uint8_t* B, const float* sB,
                            uint16_t* C, const int32_t* group_offsets, int E, int64_t M_total,
                            int64_t N, int64_t K, int64_t ld, void* stream) {

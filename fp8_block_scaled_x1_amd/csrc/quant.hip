@@ -446,6 +446,120 @@ __global__ __launch_bounds__(256) void quant_act_128x1_T_wave_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Both quantizations of one BF16 activation in one pass over it (C a multiple
+// of 256): the 128x1 groups, written transposed, exactly as the wave kernel
+// above forms them, and the 1x128 groups along each token's channels, as the
+// 1x128 kernel forms them. The backward pass needs dY both ways (1x128 for
+// Dgrad, 128x1 for Wgrad); one pass reads it once. Lane layout of the wave
+// kernel: wave w holds channels c0 .. c0+63 (c0 = 256 bx + 64 w), lane l the
+// 8 channels c0 + 8(l%8) .. of the 16 tokens 16(l/8) .. of the group. A
+// token's 128-channel group is the channels of the wave pair (2p, 2p+1): its
+// maximum is reduced over the 8 lanes that hold the token in each wave
+// (xor 1, 2, 4) and over the pair through LDS. Each lane then writes, per
+// channel, its 16 tokens' codes (16 bytes of a qT row) and, per token, its 8
+// channels' codes (8 bytes of a q row).
+// GROUPED as for the wave kernel: rows past the group's valid rows read as
+// zeros for the 128x1 groups, and are neither read as tokens of their own
+// nor written to q and s.
+// ---------------------------------------------------------------------------
+template <bool GROUPED>
+__global__ __launch_bounds__(256) void quant_act_dual_kernel(
+    const uint16_t* __restrict__ x, int64_t M, int C, uint8_t* __restrict__ q, float* __restrict__ s,
+    uint8_t* __restrict__ qT, float* __restrict__ sT, const int32_t* __restrict__ off, int E, int64_t ld) {
+  __shared__ float red[4][kGroup];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int g = blockIdx.y;
+  int64_t row0 = (int64_t)g * kGroup;   // first input row of the group
+  int n_rows = kGroup;                  // its valid rows
+  if constexpr (GROUPED) {
+    const ExpertSlot es = locate_expert(off, E, (int)M, g, kGroup, 1);
+    if (es.e < 0) return;               // past the last group (the same for every wave)
+    row0 = es.r0 + (int64_t)kGroup * (g - es.base);
+    n_rows = min(kGroup, es.r1 - (int)row0);
+  }
+  const int c0 = (blockIdx.x * 4 + w) * 64;   // C % 256 == 0: every wave has its 64 channels
+  const int ch = c0 + 8 * (lane & 7);
+  const int tb = 16 * (lane >> 3);
+
+  uint4 raw[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int r = GROUPED ? min(tb + i, n_rows - 1) : tb + i;
+    raw[i] = load16_stream(x + (row0 + r) * C + ch);
+  }
+  auto val = [&](int i, int j) {
+    const uint32_t d = word_of(raw[i], j >> 1);
+    const float f = __uint_as_float((j & 1) ? (d & 0xFFFF0000u) : (d << 16));
+    return GROUPED && tb + i >= n_rows ? 0.0f : f;
+  };
+  // 128x1: per channel, over the group's tokens
+  float sc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(val(i, j)));
+    m = fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0x128, 0xF, 0xF, false)));  // ror 8
+    m = fmaxf(m, __shfl_xor(m, 16, 64));
+    m = fmaxf(m, __shfl_xor(m, 32, 64));
+    sc[j] = scale_rule<false>(m);
+  }
+  // widen again for each later use rather than keep 128 widened values live
+#pragma unroll
+  for (int i = 0; i < 16; ++i) asm volatile("" : "+v"(raw[i].x), "+v"(raw[i].y), "+v"(raw[i].z), "+v"(raw[i].w));
+  // 1x128: per token, over the wave pair's 128 channels
+  float tm[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    float m = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(val(i, j)));
+    m = fmaxf(m, __shfl_xor(m, 1, 64));
+    m = fmaxf(m, __shfl_xor(m, 2, 64));
+    m = fmaxf(m, __shfl_xor(m, 4, 64));
+    tm[i] = m;
+  }
+  if ((lane & 7) == 0) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) red[w][tb + i] = tm[i];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 16; ++i) tm[i] = fmaxf(tm[i], red[w ^ 1][tb + i]);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) asm volatile("" : "+v"(raw[i].x), "+v"(raw[i].y), "+v"(raw[i].z), "+v"(raw[i].w));
+
+  if (lane < 8) {
+    float4* sp = reinterpret_cast<float4*>(sT + (int64_t)g * C + ch);
+    sp[0] = make_float4(sc[0], sc[1], sc[2], sc[3]);
+    sp[1] = make_float4(sc[4], sc[5], sc[6], sc[7]);
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const GroupDiv gd = div_of_scale_rule<true, false>(sc[j]);
+    uint32_t wd[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      wd[k] = pack4_rule<true, false>(val(4 * k, j), val(4 * k + 1, j), val(4 * k + 2, j), val(4 * k + 3, j), gd);
+    *reinterpret_cast<uint4*>(qT + (int64_t)(ch + j) * ld + (int64_t)g * kGroup + tb) =
+        make_uint4(wd[0], wd[1], wd[2], wd[3]);
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) asm volatile("" : "+v"(raw[i].x), "+v"(raw[i].y), "+v"(raw[i].z), "+v"(raw[i].w));
+  const int kb = c0 / kGroup;   // the 1x128 group column of this wave's channels
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    if (GROUPED && tb + i >= n_rows) continue;
+    const int64_t row = row0 + tb + i;
+    const GroupDiv gt = div_rule<true, false>(tm[i]);
+    const uint2 codes = make_uint2(pack4_rule<true, false>(val(i, 0), val(i, 1), val(i, 2), val(i, 3), gt),
+                                   pack4_rule<true, false>(val(i, 4), val(i, 5), val(i, 6), val(i, 7), gt));
+    *reinterpret_cast<uint2*>(q + row * C + ch) = codes;
+    if ((lane & 7) == 0 && (w & 1) == 0) s[(int64_t)kb * M + row] = gt.s;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Launchers (shapes validated by the C ABI layer).
 // ---------------------------------------------------------------------------
 hipError_t launch_quant_act_1x128(const void* x, bool bf16, bool pow2, int64_t M, int64_t K, uint8_t* q,
@@ -525,6 +639,27 @@ hipError_t launch_quant_act_128x1_T_grouped(const void* x, bool bf16, int64_t M_
     hipLaunchKernelGGL((quant_act_128x1_T_v8_kernel<false, true, false>), grid, dim3(256), 0, stream, x, M_total,
                        (int)C, qT, sT, offsets, E, ld);
   return hipGetLastError();
+}
+
+hipError_t launch_quant_act_dual(const void* x, bool bf16, int64_t M, int64_t C, uint8_t* q, float* s,
+                                 uint8_t* qT, float* sT, const int32_t* offsets, int E, int64_t ld,
+                                 hipStream_t stream) {
+  const bool grouped = offsets != nullptr;
+  if (bf16 && C % 256 == 0) {
+    const dim3 grid((unsigned)(C / 256), (unsigned)((grouped ? ld : M) / kGroup));
+    if (grouped)
+      hipLaunchKernelGGL((quant_act_dual_kernel<true>), grid, dim3(256), 0, stream, static_cast<const uint16_t*>(x),
+                         M, (int)C, q, s, qT, sT, offsets, E, ld);
+    else
+      hipLaunchKernelGGL((quant_act_dual_kernel<false>), grid, dim3(256), 0, stream,
+                         static_cast<const uint16_t*>(x), M, (int)C, q, s, qT, sT, nullptr, 0, M);
+    return hipGetLastError();
+  }
+  // other inputs: the two passes, one after the other
+  const hipError_t e = launch_quant_act_1x128(x, bf16, false, M, C, q, s, stream);
+  if (e != hipSuccess) return e;
+  if (grouped) return launch_quant_act_128x1_T_grouped(x, bf16, M, C, offsets, E, ld, qT, sT, stream);
+  return launch_quant_act_128x1_T(x, bf16, false, M, C, qT, sT, stream);
 }
 
 }  // namespace fp8bs

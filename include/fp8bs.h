@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define FP8BS_ABI_VERSION 10
+#define FP8BS_ABI_VERSION 11
 
 #ifndef FP8BS_API
 #define FP8BS_API __attribute__((visibility("default")))
@@ -257,6 +257,41 @@ FP8BS_API int fp8_grouped_gemm_blockscaled(const uint8_t* A, const float* sA,
 FP8BS_API int fp8_quant_act_128x1_T_grouped(const void* x, int dtype, int64_t M_total, int64_t C,
                           const int32_t* group_offsets, int E, int64_t ld,
                           uint8_t* qT, float* sT, void* stream);
+
+/*
+ * Both quantizations of one activation in a single pass over it: the 1x128
+ * groups of fp8_quant_act_1x128 (groups along each row's C values) and the
+ * 128x1 groups of fp8_quant_act_128x1_T (groups along 128 rows of one
+ * column, written transposed). The backward pass quantizes the output
+ * gradient dY both ways, 1x128 for the Dgrad GEMM and 128x1 for the Wgrad
+ * GEMM (FP8 for Fprop, Dgrad and Wgrad, report section 3.3.1, and the
+ * per-group scaling along the inner dimension of each, report section 3.3.2,
+ * on the innerforce.co.kr page); reading dY once halves the pass's input
+ * traffic. Outputs bit-identical to the two calls:
+ *   x    [M][C]        F32 or BF16 (dtype)
+ *   q    [M][C]        uint8,  s  [C/128][M] float32   (fp8_quant_act_1x128, K = C)
+ *   qT   [C][M]        uint8,  sT [M/128][C] float32   (fp8_quant_act_128x1_T)
+ * M and C multiples of 128; M == 0 or C == 0: no-op. One pass for BF16
+ * inputs with C a multiple of 256; otherwise the two passes, one after the
+ * other, on the same stream. FP8BS_ERR_TOO_LARGE beyond the limits of either
+ * call.
+ */
+FP8BS_API int fp8_quant_act_1x128_128x1_T(const void* x, int dtype, int64_t M, int64_t C,
+                          uint8_t* q, float* s, uint8_t* qT, float* sT, void* stream);
+
+/*
+ * The same in the grouped (per-expert) form: q and s as fp8_quant_act_1x128
+ * over all M_total rows, qT and sT as fp8_quant_act_128x1_T_grouped with the
+ * same group_offsets, E and ld (the MoE backward needs the experts' dY both
+ * ways: 1x128 for the grouped Dgrad, 128x1 per expert for the grouped Wgrad).
+ *   x    [M_total][C]   q [M_total][C], s [C/128][M_total]
+ *   qT   [C][ld]        sT [ld/128][C]   (columns and rows past the last group not written)
+ * C a multiple of 128; ld a multiple of 128 with ld >= M_total + 127 E;
+ * group_offsets 4-byte aligned, with the precondition of the grouped GEMM.
+ */
+FP8BS_API int fp8_quant_act_1x128_128x1_T_grouped(const void* x, int dtype, int64_t M_total, int64_t C,
+                          const int32_t* group_offsets, int E, int64_t ld,
+                          uint8_t* q, float* s, uint8_t* qT, float* sT, void* stream);
 
 /*
  * Per-expert Wgrad GEMM (the FP8 Wgrad GEMM of report sections 3.3.1-3.3.2,

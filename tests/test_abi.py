@@ -32,7 +32,8 @@ def L():
 def test_header_declares_the_entry_points():
     names = set(_declared_functions())
     assert {"fp8_quant_act_1x128", "fp8_quant_w_128x128", "fp8_quant_act_128x1_T",
-            "fp8_quant_act_128x1_T_grouped", "fp8_gemm_blockscaled", "fp8_gemm_blockscaled_q1x128",
+            "fp8_quant_act_128x1_T_grouped", "fp8_quant_act_1x128_128x1_T", "fp8_quant_act_1x128_128x1_T_grouped",
+            "fp8_gemm_blockscaled", "fp8_gemm_blockscaled_q1x128",
             "fp8_gemm_blockscaled_q1x128_q128x1T", "fp8_gemm_blockscaled_tile",
             "fp8_grouped_gemm_blockscaled", "fp8_grouped_gemm_wgrad", "fp8_moe_dispatch",
             "fp8_moe_dispatch_workspace_bytes", "fp8_moe_dispatch_noalloc", "fp8_moe_combine", "fp8_quant_act_1x128_pow2",
@@ -47,7 +48,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.fp8bs_abi_version() == fb.ABI_VERSION == 10
+    assert L.fp8bs_abi_version() == fb.ABI_VERSION == 11
     for code in range(-8, 1):
         assert fb.status_string(code) not in ("", "unknown status")
     assert fb.status_string(-99) == "unknown status"
@@ -135,6 +136,27 @@ def test_fused_epilogue_validation(L):
     assert g(P, P, P, P, 0, P, P, NULL, P, 128, 128, 128, NULL) == -1
     assert g(P, P, P, P, 0, P, P, P, MIS, 128, 128, 128, NULL) == -3
     assert g(NULL, NULL, NULL, NULL, 0, NULL, NULL, NULL, NULL, 0, 128, 128, NULL) == 0
+
+
+def test_dual_layout_quantizer_validation(L):
+    f = L.fp8_quant_act_1x128_128x1_T
+    assert f(P, 3, 128, 128, P, P, P, P, NULL) == -4                # unknown dtype
+    assert f(P, 1, 100, 128, P, P, P, P, NULL) == -2                # M not a multiple of 128
+    assert f(P, 1, 128, 100, P, P, P, P, NULL) == -2                # C not a multiple of 128
+    assert f(P, 1, 128, 128, P, P, NULL, P, NULL) == -1
+    assert f(P, 1, 128, 128, P, MIS, P, P, NULL) == -3
+    assert f(P, 1, 1 << 24, 128, P, P, P, P, NULL) == -7            # M / 128 beyond the grid
+    assert f(NULL, 1, 0, 128, NULL, NULL, NULL, NULL, NULL) == 0    # no rows: no-op
+    g = L.fp8_quant_act_1x128_128x1_T_grouped
+    ld = fb.grouped_ld(300, 2)
+    assert g(P, 1, 300, 128, P, 2, ld - 128, P, P, P, P, NULL) == -2  # ld too small for the padding
+    assert g(P, 1, 300, 100, P, 2, ld, P, P, P, P, NULL) == -2        # C not a multiple of 128
+    assert g(P, 1, 300, 128, P, 0, ld, P, P, P, P, NULL) == -2        # rows but no experts
+    assert g(P, 1, 300, 128, NULL, 2, ld, P, P, P, P, NULL) == -1
+    assert g(P, 1, 300, 128, P, 2, ld, P, NULL, P, P, NULL) == -1
+    assert g(P, 1, 300, 128, P + 2, 2, ld, P, P, P, P, NULL) == -3    # offsets not 4-byte aligned
+    assert g(P, 1, 300, 128, P, 2, ld, P, P, MIS, P, NULL) == -3
+    assert g(NULL, 1, 0, 128, NULL, 2, fb.grouped_ld(0, 2), NULL, NULL, NULL, NULL, NULL) == 0
 
 
 def test_grouped_backward_validation(L):

@@ -71,6 +71,57 @@ def test_grouped_quant_128x1_T(dev, counts, dtype, C):
     _check_grouped_quant(dev, x, counts, f"grouped 128x1 {counts} C={C} {dtype}")
 
 
+@pytest.mark.parametrize("counts", COUNTS)
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("C", [256, 384, 512])
+def test_grouped_dual_layout_quantizer(dev, counts, dtype, C):
+    # 1x128 over all rows and the grouped 128x1 in one call (one pass for
+    # BF16 with C % 256 == 0, the two passes otherwise)
+    x = _x(sum(counts), C, 7 * sum(counts) + C, dtype)
+    off = _offsets(counts)
+    offd = torch.from_numpy(off).to(dev)
+    M, E = sum(counts), len(counts)
+    ld = fb.grouped_ld(M, E)
+    q = torch.full((M, C), 0xCD, dtype=torch.uint8, device=dev)
+    s = torch.full((C // 128, M), -7.0, dtype=torch.float32, device=dev)
+    qT = torch.full((C, ld), 0xCD, dtype=torch.uint8, device=dev)
+    sT = torch.full((ld // 128, C), -7.0, dtype=torch.float32, device=dev)
+    xd = x.to(dev)
+    rc = fb.lib().fp8_quant_act_1x128_128x1_T_grouped(
+        xd.data_ptr(), fb.BF16 if x.dtype == torch.bfloat16 else fb.F32, M, C, offd.data_ptr(), E, ld,
+        q.data_ptr(), s.data_ptr(), qT.data_ptr(), sT.data_ptr(), torch.cuda.current_stream().cuda_stream)
+    assert rc == 0, fb.status_string(rc)
+    torch.cuda.synchronize()
+    what = f"grouped 1x128+128x1 {counts} C={C} {dtype}"
+    if M > 0:
+        qo, so = oracle.quant_act_1x128(to_oracle(x))
+        assert_codes_equal(u8(q), qo, f"{what}: 1x128 codes")
+        assert_scales_equal(s.cpu().numpy(), so, f"{what}: 1x128 scales")
+    q_ref, s_ref = oracle.quant_act_128x1_T_grouped(to_oracle(x), off)
+    G = s_ref.shape[0]
+    assert_codes_equal(u8(qT[:, :128 * G]), q_ref, f"{what}: 128x1 codes")
+    assert_scales_equal(sT[:G].cpu().numpy(), s_ref, f"{what}: 128x1 scales")
+    assert torch.all(qT[:, 128 * G:] == 0xCD), f"{what}: codes written past the last group"
+    assert torch.all(sT[G:] == -7.0), f"{what}: scales written past the last group"
+
+
+def test_grouped_dual_layout_quantizer_moe_workload(dev):
+    # the MoE backward's dY_down at full size (65,536 routed rows x 7,168):
+    # identical to the two separate passes
+    d = workloads.grouped_moe(device=dev, with_weights=False)
+    off = torch.from_numpy(d["offsets"]).to(dev)
+    x = d["A_up"]
+    q, s, qT, sT = fb.fp8_quant_act_1x128_128x1_T_grouped(x, off)
+    q1, s1 = fb.fp8_quant_act_1x128(x)
+    qt1, st1 = fb.fp8_quant_act_128x1_T_grouped(x, off)
+    torch.cuda.synchronize()
+    G = int(oracle.padded_group_starts(d["offsets"])[-1])
+    assert torch.equal(q, q1), "1x128 codes differ from the separate pass"
+    assert torch.equal(s.view(torch.int32), s1.view(torch.int32)), "1x128 scales differ from the separate pass"
+    assert torch.equal(qT[:, :128 * G], qt1[:, :128 * G]), "128x1 codes differ from the separate pass"
+    assert torch.equal(sT[:G].view(torch.int32), st1[:G].view(torch.int32)), "128x1 scales differ"
+
+
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 def test_grouped_quant_128x1_T_adversarial(dev, dtype):
     # the hard patterns of the quantizer tests, down the token columns of

@@ -131,6 +131,55 @@ def test_quant_act_128x1_T_backward_workload(dev):
             assert_scales_equal(sT[tb:tb + 1].cpu().numpy(), so, f"128x1 {name} scales chunk {tb}")
 
 
+def _check_dual(x_cpu, dev, what):
+    q, s, qT, sT = fb.fp8_quant_act_1x128_128x1_T(x_cpu.to(dev))
+    qo, so = oracle.quant_act_1x128(to_oracle(x_cpu))
+    qto, sto = oracle.quant_act_128x1_T(to_oracle(x_cpu))
+    torch.cuda.synchronize()
+    assert_codes_equal(q.cpu().numpy(), qo, what + " 1x128 codes")
+    assert_scales_equal(s.cpu().numpy(), so, what + " 1x128 scales")
+    assert_codes_equal(qT.cpu().numpy(), qto, what + " 128x1 codes")
+    assert_scales_equal(sT.cpu().numpy(), sto, what + " 128x1 scales")
+
+
+# C % 256 == 0 with BF16 takes the single pass; the other cases the two passes
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("M,C", [(128, 256), (256, 512), (384, 7168), (128, 384), (256, 128)])
+def test_dual_layout_quantizer(dev, dtype, M, C):
+    _check_dual(_rand((M, C), 3 * M + C, dtype), dev, f"1x128+128x1 {dtype} {M}x{C}")
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_dual_layout_quantizer_adversarial(dev, dtype):
+    # hard 1x128 groups along the rows, then hard 128x1 groups down the columns
+    rows = adversarial_rows(256, 512, seed=21)                             # [256 tokens][512 channels]
+    cols = np.ascontiguousarray(adversarial_rows(512, 256, seed=22).T)     # [256 tokens][512 channels]
+    _check_dual(torch.from_numpy(rows).to(dtype), dev, f"1x128+128x1 adversarial rows {dtype}")
+    _check_dual(torch.from_numpy(cols).to(dtype), dev, f"1x128+128x1 adversarial columns {dtype}")
+
+
+def test_dual_layout_quantizer_backward_workload(dev):
+    # full size: identical to the two separate passes (each pinned to the
+    # oracle above), and sampled token chunks against the oracle
+    d = workloads.backward_pair(device=dev)
+    dY = d["dY"]
+    q, s, qT, sT = fb.fp8_quant_act_1x128_128x1_T(dY)
+    q1, s1 = fb.fp8_quant_act_1x128(dY)
+    qt1, st1 = fb.fp8_quant_act_128x1_T(dY)
+    torch.cuda.synchronize()
+    assert torch.equal(q, q1) and torch.equal(qT, qt1), "codes differ from the separate passes"
+    assert torch.equal(s.view(torch.int32), s1.view(torch.int32)), "1x128 scales differ from the separate pass"
+    assert torch.equal(sT.view(torch.int32), st1.view(torch.int32)), "128x1 scales differ from the separate pass"
+    for tb in (0, 17, 31):
+        xs = dY[tb * 128:(tb + 1) * 128]
+        qo, so = oracle.quant_act_128x1_T(to_oracle(xs))
+        assert_codes_equal(qT[:, tb * 128:(tb + 1) * 128].cpu().numpy(), qo, f"dY 128x1 chunk {tb}")
+        assert_scales_equal(sT[tb:tb + 1].cpu().numpy(), so, f"dY 128x1 scales chunk {tb}")
+        qo, so = oracle.quant_act_1x128(to_oracle(xs))
+        assert_codes_equal(q[tb * 128:(tb + 1) * 128].cpu().numpy(), qo, f"dY 1x128 rows of chunk {tb}")
+        assert_scales_equal(s[:, tb * 128:(tb + 1) * 128].cpu().numpy(), so, f"dY 1x128 scales of chunk {tb}")
+
+
 def test_quantizers_are_deterministic(dev):
     x = _rand((512, 1024), 77, torch.bfloat16).to(dev)
     a = fb.fp8_quant_act_1x128(x)
