@@ -507,6 +507,23 @@ __global__ __launch_bounds__(256) void quant_act_dual_kernel(
   // widen again for each later use rather than keep 128 widened values live
 #pragma unroll
   for (int i = 0; i < 16; ++i) asm volatile("" : "+v"(raw[i].x), "+v"(raw[i].y), "+v"(raw[i].z), "+v"(raw[i].w));
+  if (lane < 8) {
+    float4* sp = reinterpret_cast<float4*>(sT + (int64_t)g * C + ch);
+    sp[0] = make_float4(sc[0], sc[1], sc[2], sc[3]);
+    sp[1] = make_float4(sc[4], sc[5], sc[6], sc[7]);
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const GroupDiv gd = div_of_scale_rule<true, false>(sc[j]);
+    uint32_t wd[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      wd[k] = pack4_rule<true, false>(val(4 * k, j), val(4 * k + 1, j), val(4 * k + 2, j), val(4 * k + 3, j), gd);
+    *reinterpret_cast<uint4*>(qT + (int64_t)(ch + j) * ld + (int64_t)g * kGroup + tb) =
+        make_uint4(wd[0], wd[1], wd[2], wd[3]);
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) asm volatile("" : "+v"(raw[i].x), "+v"(raw[i].y), "+v"(raw[i].z), "+v"(raw[i].w));
   // 1x128: per token, over the wave pair's 128 channels
   float tm[16];
 #pragma unroll
@@ -529,23 +546,6 @@ __global__ __launch_bounds__(256) void quant_act_dual_kernel(
 #pragma unroll
   for (int i = 0; i < 16; ++i) asm volatile("" : "+v"(raw[i].x), "+v"(raw[i].y), "+v"(raw[i].z), "+v"(raw[i].w));
 
-  if (lane < 8) {
-    float4* sp = reinterpret_cast<float4*>(sT + (int64_t)g * C + ch);
-    sp[0] = make_float4(sc[0], sc[1], sc[2], sc[3]);
-    sp[1] = make_float4(sc[4], sc[5], sc[6], sc[7]);
-  }
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const GroupDiv gd = div_of_scale_rule<true, false>(sc[j]);
-    uint32_t wd[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-      wd[k] = pack4_rule<true, false>(val(4 * k, j), val(4 * k + 1, j), val(4 * k + 2, j), val(4 * k + 3, j), gd);
-    *reinterpret_cast<uint4*>(qT + (int64_t)(ch + j) * ld + (int64_t)g * kGroup + tb) =
-        make_uint4(wd[0], wd[1], wd[2], wd[3]);
-  }
-#pragma unroll
-  for (int i = 0; i < 16; ++i) asm volatile("" : "+v"(raw[i].x), "+v"(raw[i].y), "+v"(raw[i].z), "+v"(raw[i].w));
   const int kb = c0 / kGroup;   // the 1x128 group column of this wave's channels
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
